@@ -1,0 +1,193 @@
+"""ctypes binding of libq4.so (argument marshalling only).
+
+Every function here takes torch device tensors, checks their dtypes and
+shapes, passes raw device pointers and the current HIP stream to the C ABI
+declared in include/q4.h, and raises if the library returns an error. No
+arithmetic of the method happens here; there is no CPU fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4.so")
+
+Q4_DT_F32, Q4_DT_BF16 = 0, 1
+Q4_FMT_Q4_0, Q4_FMT_AFFINE = 0, 1
+Q4_PATH_GEMV, Q4_PATH_GEMM = 0, 1
+Q4K_BLOCK_BYTES = 144
+
+EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
+           "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string")
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libq4.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with block_quantized_bit_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.q4_status_string.restype = ctypes.c_char_p
+        L.q4_status_string.argtypes = [I]
+        L.q4_quantize_act.argtypes = [I, I, I, I, P, P, P, P, P]
+        L.q4_gemv.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.q4_gemm.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.q4_debug_partials.argtypes = [I, I, I, I, I, I, I, P, P, P, I, I, P, P]
+        L.q4k_gemv.argtypes = [I, I, I, P, P, P, P]
+        L.q4k_gemm.argtypes = [I, I, I, P, P, P, P]
+        L.q4_quantize_weights.argtypes = [I, I, I, I, I, I, P, P, P, P, P]
+        L.q4k_quantize_weights.argtypes = [I, I, P, P, P]
+        for name in EXPORTS:
+            if name != "q4_status_string":
+                getattr(L, name).restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().q4_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise Q4Error(rc, what)
+
+
+def _xdtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return Q4_DT_F32
+    if t.dtype == torch.bfloat16:
+        return Q4_DT_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _fmt(fmt: str) -> int:
+    if fmt == "q4_0":
+        return Q4_FMT_Q4_0
+    if fmt == "affine":
+        return Q4_FMT_AFFINE
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+# ---- entry points --------------------------------------------------------------
+
+def quantize_act(x: torch.Tensor, bs: int, out=None, stream=None):
+    """x [M][K] float32 or bfloat16 -> (xq int8 [M][K], xs float32 [M][K/bs], xsum int32 [M][K/bs])."""
+    M, K = x.shape
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        xs = torch.empty((M, K // bs), dtype=torch.float32, device=x.device)
+        xsum = torch.empty((M, K // bs), dtype=torch.int32, device=x.device)
+    else:
+        xq, xs, xsum = out
+    _check(lib().q4_quantize_act(M, K, bs, _xdtype(x), _ptr(x), _ptr(xq), _ptr(xs), _ptr(xsum), _stream(stream)),
+           "q4_quantize_act")
+    return xq, xs, xsum
+
+
+def _matmul(entry: str, M: int, fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y, bits, stream):
+    N, Kh = wq.shape
+    K = 2 * Kh
+    if xq.shape[1] != K:
+        raise ValueError("xq and wq disagree on K")
+    _check(getattr(lib(), entry)(M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(wscale), _ptr(wbias), _ptr(xq),
+                                 _ptr(xs), _ptr(xsum), _ptr(y), _stream(stream)), entry)
+    return y
+
+
+def gemv(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int = 4, stream=None):
+    """Decode GEMV (xq is [1][K]) -> y float32 [1][N]."""
+    if y is None:
+        y = torch.empty((xq.shape[0], wq.shape[0]), dtype=torch.float32, device=wq.device)
+    return _matmul("q4_gemv", xq.shape[0], fmt, bs, wq, wscale, wbias, xq, xs, xsum, y, bits, stream)
+
+
+def gemm(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int = 4, stream=None):
+    """Prefill GEMM (xq is [M][K]) -> y float32 [M][N]."""
+    if y is None:
+        y = torch.empty((xq.shape[0], wq.shape[0]), dtype=torch.float32, device=wq.device)
+    return _matmul("q4_gemm", xq.shape[0], fmt, bs, wq, wscale, wbias, xq, xs, xsum, y, bits, stream)
+
+
+def debug_partials(path: str, fmt: str, bs: int, wq, xq, xsum, m0: int = 0, m1: int | None = None, out=None,
+                   bits: int = 4, stream=None):
+    """Exact per-block int32 partials [(m1-m0)][N][K/bs] from the GEMV ('gemv') or GEMM ('gemm') kernel."""
+    N, Kh = wq.shape
+    K = 2 * Kh
+    M = xq.shape[0]
+    m1 = M if m1 is None else m1
+    if out is None:
+        out = torch.empty((max(m1 - m0, 1), N, K // bs), dtype=torch.int32, device=wq.device)
+    p = {"gemv": Q4_PATH_GEMV, "gemm": Q4_PATH_GEMM}[path]
+    _check(lib().q4_debug_partials(p, M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(xq), _ptr(xsum), m0, m1,
+                                   _ptr(out), _stream(stream)), "q4_debug_partials")
+    return out
+
+
+def q4k_gemv(blocks, x, N: int, y=None, stream=None):
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().q4k_gemv(M, K, N, _ptr(blocks), _ptr(x), _ptr(y), _stream(stream)), "q4k_gemv")
+    return y
+
+
+def q4k_gemm(blocks, x, N: int, y=None, stream=None):
+    M, K = x.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check(lib().q4k_gemm(M, K, N, _ptr(blocks), _ptr(x), _ptr(y), _stream(stream)), "q4k_gemm")
+    return y
+
+
+def quantize_weights(w: torch.Tensor, fmt: str, bs: int, bits: int = 4, stream=None):
+    """w [N][K] float32 or bfloat16 -> (wq uint8 [N][K/2], wscale, wbias) with fp16 (Q4_0) or bf16 (affine) scales."""
+    N, K = w.shape
+    f = _fmt(fmt)
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    sdt = torch.float16 if f == Q4_FMT_Q4_0 else torch.bfloat16
+    ws = torch.empty((N, K // bs), dtype=sdt, device=w.device)
+    wb = None if f == Q4_FMT_Q4_0 else torch.empty((N, K // bs), dtype=sdt, device=w.device)
+    _check(lib().q4_quantize_weights(N, K, bs, f, bits, _xdtype(w), _ptr(w), _ptr(wq), _ptr(ws), _ptr(wb),
+                                     _stream(stream)), "q4_quantize_weights")
+    return wq, ws, wb
+
+
+def q4k_quantize_weights(w: torch.Tensor, stream=None):
+    """w [N][K] float32 -> Q4_K blocks uint8 [N][K/256*144]."""
+    N, K = w.shape
+    blocks = torch.empty((N, K // 256 * Q4K_BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    _check(lib().q4k_quantize_weights(N, K, _ptr(w), _ptr(blocks), _stream(stream)), "q4k_quantize_weights")
+    return blocks

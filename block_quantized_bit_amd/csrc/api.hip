@@ -1,0 +1,157 @@
+// C-ABI entry points: host-side argument validation, then kernel launches.
+// Validation is pure host code and runs before any HIP call, so an invalid
+// call returns its status without touching the device.
+#include <stdint.h>
+
+#include "q4.h"
+#include "kernels.h"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int block_status(int K, int bs, int fmt) {
+    if (fmt == Q4_FMT_Q4_0) {
+        if (bs != 32) return Q4_ERR_BLOCK;
+    } else if (fmt == Q4_FMT_AFFINE) {
+        if (bs != 64 && bs != 128) return Q4_ERR_BLOCK;
+    } else {
+        return Q4_ERR_FORMAT;
+    }
+    if (K % bs != 0) return Q4_ERR_BLOCK;
+    return Q4_OK;
+}
+
+// Common checks of the W4A8 matmul entry points (pointers checked by callers).
+int matmul_status(int M, int K, int N, int bs, int fmt, int bits) {
+    if (bits != 4) return Q4_ERR_FORMAT;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE) return Q4_ERR_FORMAT;
+    if (M <= 0 || N <= 0 || K <= 0) return Q4_ERR_DIM;
+    return block_status(K, bs, fmt);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_status_string(int status) {
+    switch (status) {
+        case Q4_OK: return "ok";
+        case Q4_ERR_NULL: return "a required pointer is NULL";
+        case Q4_ERR_DIM: return "M, N or K out of range";
+        case Q4_ERR_BLOCK: return "K is not a multiple of the block size, or the block size is invalid for the format";
+        case Q4_ERR_FORMAT: return "unknown format or dtype, or a bit width other than 4 (these kernels decode two 4-bit codes per byte)";
+        case Q4_ERR_ALIGN: return "a pointer is not aligned as its argument requires";
+        case Q4_ERR_HIP: return "a kernel launch failed";
+        case Q4_ERR_RANGE: return "row range [m0, m1) is empty or outside [0, M]";
+        default: return "unknown status";
+    }
+}
+
+int q4_quantize_act(int M, int K, int bs, int xdtype, const void* x, int8_t* xq, float* xs, int32_t* xsum,
+                    void* stream) {
+    if (!x || !xq || !xs || !xsum) return Q4_ERR_NULL;
+    if (xdtype != Q4_DT_F32 && xdtype != Q4_DT_BF16) return Q4_ERR_FORMAT;
+    if (M <= 0 || K <= 0) return Q4_ERR_DIM;
+    if ((bs != 32 && bs != 64 && bs != 128) || K % bs != 0) return Q4_ERR_BLOCK;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(xs, 4) || !aligned(xsum, 4)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_quantize_act(M, K, bs, xdtype == Q4_DT_BF16, x, xq, xs, xsum,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+static int check_matmul_ptrs(int fmt, const uint8_t* wq, const void* wscale, const void* wbias, const int8_t* xq,
+                             const float* xs, const int32_t* xsum, const void* out) {
+    if (!wq || !wscale || !xq || !xs || !xsum || !out) return Q4_ERR_NULL;
+    if (fmt == Q4_FMT_AFFINE && !wbias) return Q4_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(wscale, 2) || (wbias && !aligned(wbias, 2)) ||
+        !aligned(xs, 4) || !aligned(xsum, 4) || !aligned(out, 4))
+        return Q4_ERR_ALIGN;
+    return Q4_OK;
+}
+
+int q4_gemv(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale, const void* wbias,
+            const int8_t* xq, const float* xs, const int32_t* xsum, float* y, void* stream) {
+    int st = matmul_status(M, K, N, bs, fmt, bits);
+    if (st) return st;
+    if (M != 1) return Q4_ERR_DIM;
+    st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
+    if (st) return st;
+    return hip_status(q4::launch_gemv(K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale, const void* wbias,
+            const int8_t* xq, const float* xs, const int32_t* xsum, float* y, void* stream) {
+    int st = matmul_status(M, K, N, bs, fmt, bits);
+    if (st) return st;
+    if (M > (1 << 23)) return Q4_ERR_DIM;  // grid rows of 128
+    st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
+    if (st) return st;
+    return hip_status(q4::launch_gemm(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const int8_t* xq,
+                      const int32_t* xsum, int m0, int m1, int32_t* partials, void* stream) {
+    int st = matmul_status(M, K, N, bs, fmt, bits);
+    if (st) return st;
+    if (path != Q4_PATH_GEMV && path != Q4_PATH_GEMM) return Q4_ERR_FORMAT;
+    if (!wq || !xq || !xsum || !partials) return Q4_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(xsum, 4) || !aligned(partials, 4)) return Q4_ERR_ALIGN;
+    if (m0 < 0 || m1 > M || m0 >= m1) return Q4_ERR_RANGE;
+    if (m1 - m0 > (1 << 23)) return Q4_ERR_DIM;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int ng = K / bs;
+    const int8_t* xq0 = xq + (size_t)m0 * K;
+    const int32_t* xsum0 = xsum + (size_t)m0 * ng;
+    if (path == Q4_PATH_GEMV) {
+        if (m1 - m0 != 1) return Q4_ERR_RANGE;
+        return hip_status(q4::launch_gemv(K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
+                                          partials, s));
+    }
+    return hip_status(q4::launch_gemm(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
+                                      partials, s));
+}
+
+int q4k_gemv(int M, int K, int N, const void* blocks, const float* x, float* y, void* stream) {
+    if (!blocks || !x || !y) return Q4_ERR_NULL;
+    if (M != 1 || N <= 0 || K <= 0) return Q4_ERR_DIM;
+    if (K % 256 != 0) return Q4_ERR_BLOCK;
+    if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_q4k_gemv(K, N, blocks, x, y, static_cast<hipStream_t>(stream)));
+}
+
+int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, void* stream) {
+    if (!blocks || !x || !y) return Q4_ERR_NULL;
+    if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 20)) return Q4_ERR_DIM;  // grid rows of 16
+    if (K % 256 != 0) return Q4_ERR_BLOCK;
+    if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_q4k_gemm(M, K, N, blocks, x, y, static_cast<hipStream_t>(stream)));
+}
+
+int q4_quantize_weights(int N, int K, int bs, int fmt, int bits, int wdtype, const void* w, uint8_t* wq,
+                        void* wscale, void* wbias, void* stream) {
+    if (bits != 4) return Q4_ERR_FORMAT;
+    if (wdtype != Q4_DT_F32 && wdtype != Q4_DT_BF16) return Q4_ERR_FORMAT;
+    if (N <= 0 || K <= 0) return Q4_ERR_DIM;
+    int st = block_status(K, bs, fmt);
+    if (st) return st;
+    if (!w || !wq || !wscale || (fmt == Q4_FMT_AFFINE && !wbias)) return Q4_ERR_NULL;
+    if (!aligned(w, wdtype == Q4_DT_F32 ? 4 : 2) || !aligned(wq, 16) || !aligned(wscale, 2) ||
+        (wbias && !aligned(wbias, 2)))
+        return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_quantize_weights(N, K, bs, fmt, wdtype == Q4_DT_BF16, w, wq, wscale, wbias,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int q4k_quantize_weights(int N, int K, const float* w, void* blocks, void* stream) {
+    if (!w || !blocks) return Q4_ERR_NULL;
+    if (N <= 0 || K <= 0) return Q4_ERR_DIM;
+    if (K % 256 != 0) return Q4_ERR_BLOCK;
+    if (!aligned(w, 4) || !aligned(blocks, 16)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_q4k_quantize_weights(N, K, w, blocks, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

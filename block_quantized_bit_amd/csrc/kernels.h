@@ -1,0 +1,30 @@
+// Internal launchers of the gfx950 kernels. Arguments are validated by the
+// C-ABI layer (api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4 {
+
+hipError_t launch_quantize_act(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs,
+                               int32_t* xsum, hipStream_t stream);
+
+// fmt: 0 = Q4_0 (bs 32), 1 = affine (bs 64 / 128). partials != nullptr selects
+// the integer-partials store in place of the float epilogue.
+hipError_t launch_gemv(int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale, const void* wbias,
+                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                       const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
+                       int32_t* partials, hipStream_t stream);
+
+hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
+hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
+
+hipError_t launch_quantize_weights(int N, int K, int bs, int fmt, bool bf16, const void* w, uint8_t* wq,
+                                   void* wscale, void* wbias, hipStream_t stream);
+hipError_t launch_q4k_quantize_weights(int N, int K, const float* w, void* blocks, hipStream_t stream);
+
+}  // namespace q4

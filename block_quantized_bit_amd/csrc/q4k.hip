@@ -1,0 +1,267 @@
+// Q4_K fused-dequant GEMV and GEMM with float32 activations.
+//
+// C-Kernel-Engine gemm_kernels_q4k.c: weights are dequantized in registers
+// and used at once by the multiply-add, never written to memory; the GEMV
+// (one token) is memory-bound, the GEMM reuses each dequantized weight for
+// every activation row. Weight value: d * sc[s] * q - dmin * m[s].
+//
+// Block: 144 bytes = 16-byte header {fp16 d, fp16 dmin, 12 bytes of 6-bit
+// scales and mins} + qs[128]. A 16-byte qs chunk j (0..7) of a block holds,
+// for chunk c = j / 2 of 64 weights and l0 = 16 * (j % 2), the 16 weights
+// 64c + l0 + t in its low nibbles (sub-block 2c) and 64c + 32 + l0 + t in its
+// high nibbles (sub-block 2c + 1).
+#include "common.h"
+#include "kernels.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int QK = 256;
+constexpr int BLOCK_BYTES = 144;
+
+// 6-bit fields of the header: sc[s] at bit 6s and m[s] at bit 48 + 6s of the
+// 96-bit little-endian string (hdr.y, hdr.z, hdr.w). Returns sc[2c], sc[2c+1],
+// m[2c], m[2c+1] as floats.
+__device__ __forceinline__ void q4k_pair_scales(const uint4& hdr, int c, float& sc0, float& sc1, float& m0,
+                                                float& m1) {
+    const uint64_t lo = (uint64_t)hdr.y | ((uint64_t)hdr.z << 32);   // bits 0..63
+    const uint64_t hi = (uint64_t)hdr.z | ((uint64_t)hdr.w << 32);   // bits 32..95
+    const uint32_t s = (uint32_t)(lo >> (12 * c)) & 0xFFFu;
+    const uint32_t m = (uint32_t)(hi >> (16 + 12 * c)) & 0xFFFu;
+    sc0 = (float)(s & 63u);
+    sc1 = (float)(s >> 6);
+    m0 = (float)(m & 63u);
+    m1 = (float)(m >> 6);
+}
+
+__device__ __forceinline__ float byte_f(uint32_t v, int b) { return (float)((v >> (8 * b)) & 0xFFu); }
+
+// Sum over 16 weights of code * x for the 4 dwords `q` (nibbles already
+// isolated into bytes) against 16 activations.
+__device__ __forceinline__ float dot16(const uint32_t q[4], const float* x) {
+    float a = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) a = fmaf(byte_f(q[t], b), x[4 * t + b], a);
+    return a;
+}
+
+// GEMV: wavefronts walk rows (R rows per pass, loads of all R rows issued
+// before any arithmetic). Lane l owns qs chunks u = l + 64 i of every row; the
+// activations of its chunks (and their sums per half) are loaded once and stay
+// in registers. UPL = chunks per lane (K / 2048, rounded up).
+template <int UPL, int R>
+__global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, const uint8_t* __restrict__ blocks,
+                                                       const float* __restrict__ x, float* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nwaves = gridDim.x * 4;
+    const int units = K >> 5;
+    const int nsb = K >> 8;
+    const int j = lane & 7;  // qs chunk within a block (u % 8 == lane % 8)
+    const int c = j >> 1, l0 = 16 * (j & 1);
+
+    float xl[UPL][16], xh[UPL][16], sl[UPL], sh[UPL];
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+        const int u = lane + 64 * i;
+        sl[i] = sh[i] = 0.0f;
+        if (u < units) {
+            const int k = (u >> 3) * QK + 64 * c + l0;
+            const float4* pl = reinterpret_cast<const float4*>(x + k);
+            const float4* ph = reinterpret_cast<const float4*>(x + k + 32);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float4 a = pl[t], b = ph[t];
+                xl[i][4 * t] = a.x; xl[i][4 * t + 1] = a.y; xl[i][4 * t + 2] = a.z; xl[i][4 * t + 3] = a.w;
+                xh[i][4 * t] = b.x; xh[i][4 * t + 1] = b.y; xh[i][4 * t + 2] = b.z; xh[i][4 * t + 3] = b.w;
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                sl[i] += xl[i][t];
+                sh[i] += xh[i][t];
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) xl[i][t] = xh[i][t] = 0.0f;
+        }
+    }
+
+    for (int nb = gw * R; nb < N; nb += nwaves * R) {
+        uint4 hdr[R][UPL], qs[R][UPL];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) {
+                const int n = nb + r, u = lane + 64 * i;
+                if (n < N && u < units) {
+                    const uint8_t* blk = blocks + ((size_t)n * nsb + (u >> 3)) * BLOCK_BYTES;
+                    hdr[r][i] = *reinterpret_cast<const uint4*>(blk);
+                    qs[r][i] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * j);
+                } else {
+                    hdr[r][i] = make_uint4(0, 0, 0, 0);
+                    qs[r][i] = hdr[r][i];
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) {
+                const float d = half_to_float(hdr[r][i].x & 0xFFFFu);
+                const float dmin = half_to_float(hdr[r][i].x >> 16);
+                float sc0, sc1, mm0, mm1;
+                q4k_pair_scales(hdr[r][i], c, sc0, sc1, mm0, mm1);
+                const uint32_t ql[4] = {lo_nibbles(qs[r][i].x), lo_nibbles(qs[r][i].y), lo_nibbles(qs[r][i].z),
+                                        lo_nibbles(qs[r][i].w)};
+                const uint32_t qh[4] = {hi_nibbles(qs[r][i].x), hi_nibbles(qs[r][i].y), hi_nibbles(qs[r][i].z),
+                                        hi_nibbles(qs[r][i].w)};
+                const float al = dot16(ql, xl[i]);
+                const float ah = dot16(qh, xh[i]);
+                acc += (d * sc0) * al - (dmin * mm0) * sl[i];
+                acc += (d * sc1) * ah - (dmin * mm1) * sh[i];
+            }
+            acc = wave_sum(acc);
+            if (lane == 0 && nb + r < N) y[nb + r] = acc;
+        }
+    }
+}
+
+// GEMV for long rows: the activations are read per row instead of being held
+// in registers.
+__global__ __launch_bounds__(256) void q4k_gemv_long_kernel(int K, int N, const uint8_t* __restrict__ blocks,
+                                                            const float* __restrict__ x, float* __restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= N) return;
+    const int units = K >> 5, nsb = K >> 8;
+    const int j = lane & 7, c = j >> 1, l0 = 16 * (j & 1);
+    float acc = 0.0f;
+    for (int u = lane; u < units; u += 64) {
+        const uint8_t* blk = blocks + ((size_t)n * nsb + (u >> 3)) * BLOCK_BYTES;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+        const uint4 q = *reinterpret_cast<const uint4*>(blk + 16 + 16 * j);
+        const int k = (u >> 3) * QK + 64 * c + l0;
+        float xl[16], xh[16], sl = 0.0f, sh = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            xl[t] = x[k + t];
+            xh[t] = x[k + 32 + t];
+            sl += xl[t];
+            sh += xh[t];
+        }
+        const float d = half_to_float(hdr.x & 0xFFFFu), dmin = half_to_float(hdr.x >> 16);
+        float sc0, sc1, mm0, mm1;
+        q4k_pair_scales(hdr, c, sc0, sc1, mm0, mm1);
+        const uint32_t ql[4] = {lo_nibbles(q.x), lo_nibbles(q.y), lo_nibbles(q.z), lo_nibbles(q.w)};
+        const uint32_t qh[4] = {hi_nibbles(q.x), hi_nibbles(q.y), hi_nibbles(q.z), hi_nibbles(q.w)};
+        acc += (d * sc0) * dot16(ql, xl) - (dmin * mm0) * sl;
+        acc += (d * sc1) * dot16(qh, xh) - (dmin * mm1) * sh;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) y[n] = acc;
+}
+
+// GEMM on the float32 matrix cores (v_mfma_f32_16x16x4_f32). A workgroup of
+// 4 wavefronts covers 16 activation rows x 64 weight rows; each wavefront owns
+// 16 weight rows. For every super-block the 16 x 256 activation tile is staged
+// in LDS; lane l dequantizes chunk h = l / 16 (64 weights: 32 low nibbles of
+// sub-block 2h, then 32 high nibbles of sub-block 2h + 1) of weight row l % 16
+// and feeds one weight per MFMA; the 4 lane groups are the MFMA's 4 K slots,
+// so one MFMA takes weights 64h + t of the block for h = 0..3.
+constexpr int XS_STRIDE = QK + 4;  // floats; keeps 16-byte alignment and spreads rows over the banks
+
+__global__ __launch_bounds__(256) void q4k_gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ blocks,
+                                                       const float* __restrict__ x, float* __restrict__ y) {
+    __shared__ __attribute__((aligned(16))) float xs[16 * XS_STRIDE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int m0 = blockIdx.y * 16;
+    const int n = blockIdx.x * 64 + wave * 16 + (lane & 15);
+    const int h = lane >> 4;
+    const int nsb = K >> 8;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int sb = 0; sb < nsb; ++sb) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i;  // 1024 float4 = 16 rows x 64
+            const int r = idx >> 6, c4 = idx & 63;
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (m0 + r < M) v = *reinterpret_cast<const float4*>(x + (size_t)(m0 + r) * K + sb * QK + 4 * c4);
+            *reinterpret_cast<float4*>(&xs[r * XS_STRIDE + 4 * c4]) = v;
+        }
+        uint4 hdr = make_uint4(0, 0, 0, 0), q0 = hdr, q1 = hdr;
+        if (n < N) {
+            const uint8_t* blk = blocks + ((size_t)n * nsb + sb) * BLOCK_BYTES;
+            hdr = *reinterpret_cast<const uint4*>(blk);
+            q0 = *reinterpret_cast<const uint4*>(blk + 16 + 32 * h);
+            q1 = *reinterpret_cast<const uint4*>(blk + 32 + 32 * h);
+        }
+        __syncthreads();
+        const float d = half_to_float(hdr.x & 0xFFFFu), dmin = half_to_float(hdr.x >> 16);
+        float sc0, sc1, mm0, mm1;
+        q4k_pair_scales(hdr, h, sc0, sc1, mm0, mm1);
+        const float ds0 = d * sc0, dm0 = dmin * mm0, ds1 = d * sc1, dm1 = dmin * mm1;
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const float* xr = &xs[(lane & 15) * XS_STRIDE + 64 * h];
+#pragma unroll
+        for (int t4 = 0; t4 < 8; ++t4) {  // low nibbles: weights 64h + 0..31
+            const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * t4);
+            const uint32_t ql = lo_nibbles(qw[t4]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, fmaf(ds0, byte_f(ql, 0), -dm0), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, fmaf(ds0, byte_f(ql, 1), -dm0), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, fmaf(ds0, byte_f(ql, 2), -dm0), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, fmaf(ds0, byte_f(ql, 3), -dm0), acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t4 = 0; t4 < 8; ++t4) {  // high nibbles: weights 64h + 32..63
+            const float4 xv = *reinterpret_cast<const float4*>(xr + 32 + 4 * t4);
+            const uint32_t qh = hi_nibbles(qw[t4]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, fmaf(ds1, byte_f(qh, 0), -dm1), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, fmaf(ds1, byte_f(qh, 1), -dm1), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, fmaf(ds1, byte_f(qh, 2), -dm1), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, fmaf(ds1, byte_f(qh, 3), -dm1), acc, 0, 0, 0);
+        }
+    }
+    // D layout of the 16x16 MFMA: lane holds column lane % 16, rows 4 * (lane / 16) + r.
+    if (n < N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * h + r;
+            if (m < M) y[(size_t)m * N + n] = acc[r];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream) {
+    const uint8_t* b = static_cast<const uint8_t*>(blocks);
+    const int units = K >> 5;
+    const int upl = (units + 63) / 64;
+    constexpr int R = 4;
+    const int rows_per_pass_blocks = (N + 4 * R - 1) / (4 * R);
+    const unsigned grid = (unsigned)min(rows_per_pass_blocks, 1024);
+    switch (upl) {
+        case 1: hipLaunchKernelGGL((q4k_gemv_kernel<1, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
+        case 2: hipLaunchKernelGGL((q4k_gemv_kernel<2, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
+        case 3: hipLaunchKernelGGL((q4k_gemv_kernel<3, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
+        case 4: hipLaunchKernelGGL((q4k_gemv_kernel<4, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
+        default:
+            hipLaunchKernelGGL(q4k_gemv_long_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, K, N, b, x,
+                               y);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16));
+    hipLaunchKernelGGL(q4k_gemm_kernel, grid, dim3(256), 0, stream, M, K, N, static_cast<const uint8_t*>(blocks), x,
+                       y);
+    return hipGetLastError();
+}
+
+}  // namespace q4

@@ -1,0 +1,177 @@
+/*
+ * q4.h -- C ABI of the gfx950 (MI355X) block-quantized 4-bit matmul library.
+ *
+ * The library computes matrix products with 4-bit block-quantized weights:
+ *   - W4A8: Q4_0 weights (32-weight blocks, one fp16 scale d each, value
+ *     d * (q - 8)) or affine 4-bit weights (groups of 64 or 128 weights with a
+ *     bf16 scale s and bias b, value s * q + b), times activations quantized
+ *     per block to int8. Each block's dot product is an exact integer; the
+ *     per-block float rescale (and, for affine weights, bias * sum x) is
+ *     applied in the kernel; the output is float32.
+ *     (tract PR #2432 "WIP: W4A8 (Q4_0 int8-dot) path for block_quant",
+ *     section "The kernel" and its pipeline figure; MLX PR #4802, mx.qqmm with
+ *     mode="affine": int8 x int8 MMA over the original codes with per-group
+ *     scales and biases applied in the kernel.)
+ *   - Q4_K: 256-weight super-blocks times float32 activations with the
+ *     dequantization fused into the multiply-add (C-Kernel-Engine
+ *     gemm_kernels_q4k.c: gemv_q4_k_ref, gemm_q4_k_ref, gemm_nt_q4_k).
+ *
+ * Conventions for every entry point
+ *   - Shapes: X is [M][K], W is [N][K], Y is [M][N], all row-major (the
+ *     gemm_nt_q4_k convention: A [M x K] activations, B [N x K] weights,
+ *     C [M x N] output). M, N >= 1; K a positive multiple of the block size.
+ *   - Memory: every pointer is a DEVICE pointer owned by the caller. The
+ *     library never allocates or frees memory and keeps no per-call state.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream). Each
+ *     call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns; results are valid once the caller synchronizes
+ *     the stream. Calls are deterministic (no float atomics).
+ *   - Errors: an invalid call returns a nonzero q4_status and enqueues
+ *     nothing. Q4_ERR_HIP reports a failed kernel launch. q4_status_string()
+ *     names a status.
+ *   - Bit width: `bits` must be 4. Any other value is rejected with
+ *     Q4_ERR_FORMAT: these kernels decode two codes per byte, and a wider
+ *     format passed to them would be decoded wrongly without any other sign
+ *     (meTile PR #29, "Measure the int8 multi-row headroom, and keep the
+ *     four-bit guard that was protecting us").
+ *
+ * Packed weight layout (shared by Q4_0 and affine)
+ *   wq [N][K/2] bytes. Block b (32 weights) of row n is the 16 bytes at
+ *   wq + n*K/2 + 16*b; byte j holds the code of k = 32*b + j in its low nibble
+ *   and of k = 32*b + 16 + j in its high nibble. An affine group of g weights
+ *   is g/32 consecutive blocks.
+ *
+ * Q4_K block layout (144 bytes, 4.5 bits per weight)
+ *   { fp16 d; fp16 dmin; uint8 scales[12]; uint8 qs[128]; }, blocks [N][K/256].
+ *   scales holds sixteen 6-bit fields, little-endian, field f at bits
+ *   [6f, 6f+6): f < 8 is the scale sc[f] of sub-block f, f >= 8 the min
+ *   m[f-8]. Chunk c (0..3) of 64 weights uses qs[32c .. 32c+31]: weight
+ *   64c + l is the low nibble of qs[32c + l] (sub-block 2c), weight
+ *   64c + 32 + l its high nibble (sub-block 2c+1). Weight value
+ *   d * sc[s] * q - dmin * m[s].
+ */
+#ifndef Q4_H
+#define Q4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q4_OK = 0,
+    Q4_ERR_NULL = 1,     /* a required pointer is NULL */
+    Q4_ERR_DIM = 2,      /* M, N or K out of range (<= 0, or an entry point's limit) */
+    Q4_ERR_BLOCK = 3,    /* K not a multiple of the block size, or block size invalid for the format */
+    Q4_ERR_FORMAT = 4,   /* unknown format or dtype, or bits != 4 */
+    Q4_ERR_ALIGN = 5,    /* a pointer is not aligned as its argument requires */
+    Q4_ERR_HIP = 6,      /* a kernel launch failed */
+    Q4_ERR_RANGE = 7     /* row range [m0, m1) outside [0, M] or empty */
+} q4_status;
+
+enum { Q4_DT_F32 = 0, Q4_DT_BF16 = 1 };
+enum {
+    Q4_FMT_Q4_0 = 0,     /* bs = 32; wscale fp16 [N][K/32]; wbias unused (may be NULL) */
+    Q4_FMT_AFFINE = 1    /* bs = g in {64, 128}; wscale, wbias bf16 [N][K/g] */
+};
+enum { Q4_PATH_GEMV = 0, Q4_PATH_GEMM = 1 };
+
+/*
+ * Per-block int8 quantization of activations (tract PR #2432: "activation ->
+ * int8, per-block"; MLX PR #4802: "x is quantized to int8").
+ * For every row m and block b of bs consecutive k:
+ *   amax = max |x|;  xs = amax / 127 (float32, correctly rounded);
+ *   xq = clamp(round_half_even(x / xs), -127, 127) with a correctly rounded
+ *   float32 quotient (all codes 0 and xs = 0 when amax == 0);
+ *   xsum = sum of the block's codes.
+ * x     [M][K], float32 (xdtype Q4_DT_F32) or bfloat16 (Q4_DT_BF16); 16-byte aligned.
+ * xq    [M][K] int8, 16-byte aligned.   xs [M][K/bs] float32.   xsum [M][K/bs] int32.
+ * bs in {32, 64, 128}.
+ */
+int q4_quantize_act(int M, int K, int bs, int xdtype, const void* x,
+                     int8_t* xq, float* xs, int32_t* xsum, void* stream);
+
+/*
+ * Decode GEMV (M must be 1): y[n] = sum over blocks b of the rescaled exact
+ * integer dot of weight row n with the int8 activation codes.
+ *   Q4_0:   y += d[n,b] * xs[b] * sum_{k in b} (q - 8) * xq
+ *   affine: y += xs[g] * (s[n,g] * sum_{k in g} q * xq + b[n,g] * xsum[g])
+ * The weight codes are streamed with 128-bit loads and the dots use the
+ * int8 dot-product instruction; one wavefront reduces each output.
+ * wq [N][K/2] (16-byte aligned), wscale/wbias as in the format enum,
+ * xq [1][K] (16-byte aligned), xs, xsum [1][K/bs] from q4_quantize_act,
+ * y [1][N] float32.
+ */
+int q4_gemv(int M, int K, int N, int bs, int fmt, int bits,
+            const uint8_t* wq, const void* wscale, const void* wbias,
+            const int8_t* xq, const float* xs, const int32_t* xsum,
+            float* y, void* stream);
+
+/*
+ * Prefill GEMM, any M >= 1: Y[m][n] as q4_gemv for every row m, computed on
+ * the int8 matrix cores (32x32x32 int8 MFMA, one 32-weight block per K-step,
+ * int32 accumulation within a block or group, float rescale per block).
+ * Same arguments as q4_gemv with xq [M][K], xs, xsum [M][K/bs], y [M][N].
+ */
+int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
+            const uint8_t* wq, const void* wscale, const void* wbias,
+            const int8_t* xq, const float* xs, const int32_t* xsum,
+            float* y, void* stream);
+
+/*
+ * Debug view of the exact integer partials computed inside q4_gemv
+ * (path Q4_PATH_GEMV, needs M == 1) or q4_gemm (Q4_PATH_GEMM): the same
+ * kernels, compiled with the partials store in place of the float epilogue.
+ * partials [(m1-m0)][N][K/bs] int32 for rows m0 <= m < m1:
+ *   Q4_0:   sum_{k in b} (q - 8) * xq[m][k]
+ *   affine: sum_{k in g} q * xq[m][k]
+ * xsum is read by the Q4_0 GEMV (which forms sum q*xq - 8*xsum); it must be
+ * the xsum of xq.
+ */
+int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits,
+                      const uint8_t* wq, const int8_t* xq, const int32_t* xsum,
+                      int m0, int m1, int32_t* partials, void* stream);
+
+/*
+ * Q4_K fused-dequant GEMV (M must be 1) and GEMM (any M >= 1) with float32
+ * activations (C-Kernel-Engine gemm_kernels_q4k.c: gemv_q4_k_ref computes
+ * sum_k (d*sc*q - dmin*m) * x per output row; gemm_q4_k_ref is one GEMV per
+ * activation row). Dequantized weights live only in registers.
+ * blocks [N][K/256] x 144 bytes (16-byte aligned), x [M][K] float32
+ * (16-byte aligned), y [M][N] float32. K must be a multiple of 256.
+ */
+int q4k_gemv(int M, int K, int N, const void* blocks, const float* x, float* y,
+             void* stream);
+int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y,
+             void* stream);
+
+/*
+ * Weight quantization on the GPU (model preparation, not the hot path).
+ * q4_quantize_weights: w [N][K] float32 or bfloat16 (wdtype) ->
+ *   Q4_0 (bs 32):  i = first index of the largest |w| in the block,
+ *                  d = fp16(w[i] / -8), q = clamp(round_half_even(w / d) + 8, 0, 15)
+ *                  (q = 8 when d == 0);
+ *   affine (bs g): s = bf16((max - min) / 15), b = bf16(min),
+ *                  q = clamp(round_half_even((w - b) / s), 0, 15) (q = 0 when s == 0);
+ *   every step in float32. wq as above (16-byte aligned); wscale, wbias as in
+ *   the format enum (wbias unused for Q4_0).
+ * q4k_quantize_weights: w [N][K] float32 -> Q4_K blocks. For each 32-weight
+ *   sub-block: lo = min(0, min w), hi = max w, a = (hi - lo) / 15, c = -lo;
+ *   d = fp16(max a / 63), dmin = fp16(max c / 63); sc = round_half_even(a / d),
+ *   m = round_half_even(c / dmin), clamped to 0..63 (0 when the divisor is 0);
+ *   q = clamp(round_half_even((w + dmin*m) / (d*sc)), 0, 15) (0 when d*sc == 0).
+ */
+int q4_quantize_weights(int N, int K, int bs, int fmt, int bits, int wdtype,
+                        const void* w, uint8_t* wq, void* wscale, void* wbias,
+                        void* stream);
+int q4k_quantize_weights(int N, int K, const float* w, void* blocks, void* stream);
+
+/* Static name of a q4_status value ("unknown status" otherwise). */
+const char* q4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_H */

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/q4.h declares, and rejects invalid calls on the host with the
+documented status before any device work (no compute call is made here).
+
+The bit-width guard follows meTile PR #29 ("keep the four-bit guard that was
+protecting us"): a four-bit-only decoder handed another width reads the data
+wrongly without failing, so the guard is load-bearing and pinned by a test.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_quantized_bit_amd as q4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, DIM, BLOCK, FORMAT, ALIGN, HIP, RANGE = range(8)
+# stand-ins for device pointers: never dereferenced, every call below fails validation first
+A = 0x100000
+MIS = 0x100001
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "q4.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(q4k?_\w+)\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    L = q4.lib()
+    names = declared_functions()
+    assert len(names) == 9
+    assert sorted(q4.EXPORTS) == names
+    for name in names:
+        assert getattr(L, name) is not None
+
+
+def test_status_strings():
+    assert q4.status_string(OK) == "ok"
+    assert "4-bit" in q4.status_string(FORMAT)
+    assert q4.status_string(99) == "unknown status"
+
+
+def gemm_args(**kw):
+    a = dict(M=4, K=128, N=8, bs=32, fmt=0, bits=4, wq=A, ws=A, wb=None, xq=A, xs=A, xsum=A, y=A)
+    a.update(kw)
+    return (a["M"], a["K"], a["N"], a["bs"], a["fmt"], a["bits"], a["wq"], a["ws"], a["wb"], a["xq"], a["xs"],
+            a["xsum"], a["y"], None)
+
+
+@pytest.mark.parametrize("entry", ["q4_gemm", "q4_gemv"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=8), FORMAT), (dict(bits=2), FORMAT), (dict(bits=6), FORMAT),
+    (dict(fmt=2), FORMAT),
+    (dict(M=0), DIM), (dict(N=0), DIM), (dict(K=0), DIM), (dict(N=-3), DIM),
+    (dict(K=100), BLOCK), (dict(bs=64), BLOCK), (dict(fmt=1, bs=32, wb=A), BLOCK),
+    (dict(fmt=1, bs=256, K=256, wb=A), BLOCK), (dict(fmt=1, bs=64, K=96, wb=A), BLOCK),
+    (dict(wq=None), NULL), (dict(ws=None), NULL), (dict(xq=None), NULL), (dict(xs=None), NULL),
+    (dict(xsum=None), NULL), (dict(y=None), NULL), (dict(fmt=1, bs=64, wb=None), NULL),
+    (dict(wq=MIS), ALIGN), (dict(xq=A + 8), ALIGN), (dict(y=MIS), ALIGN), (dict(xs=A + 2), ALIGN),
+])
+def test_matmul_validation(entry, kw, status):
+    if entry == "q4_gemv" and "M" not in kw:
+        kw = dict(kw, M=1)
+    args = gemm_args(**kw)
+    assert getattr(q4.lib(), entry)(*args) == status
+
+
+def test_gemv_requires_one_row():
+    assert q4.lib().q4_gemv(*gemm_args(M=2)) == DIM
+
+
+def test_quantize_act_validation():
+    f = q4.lib().q4_quantize_act
+    assert f(4, 128, 32, 0, None, A, A, A, None) == NULL
+    assert f(4, 128, 32, 2, A, A, A, A, None) == FORMAT
+    assert f(0, 128, 32, 0, A, A, A, A, None) == DIM
+    assert f(4, 100, 32, 0, A, A, A, A, None) == BLOCK
+    assert f(4, 128, 48, 0, A, A, A, A, None) == BLOCK
+    assert f(4, 128, 32, 1, A + 4, A, A, A, None) == ALIGN
+    assert f(4, 128, 32, 1, A, A + 1, A, A, None) == ALIGN
+
+
+def test_debug_partials_validation():
+    f = q4.lib().q4_debug_partials
+    base = [1, 4, 128, 8, 32, 0, 4, A, A, A, 0, 4, A, None]
+    assert f(*base[:6], 8, *base[7:]) == FORMAT          # bits
+    assert f(2, *base[1:]) == FORMAT                     # path
+    args = list(base); args[10], args[11] = 2, 2
+    assert f(*args) == RANGE                             # empty range
+    args = list(base); args[11] = 5
+    assert f(*args) == RANGE                             # beyond M
+    args = list(base); args[0] = 0
+    assert f(*args) == RANGE                             # GEMV path needs one row
+    args = list(base); args[12] = None
+    assert f(*args) == NULL
+
+
+def test_q4k_validation():
+    for f in (q4.lib().q4k_gemv, q4.lib().q4k_gemm):
+        assert f(1, 4096, 8, None, A, A, None) == NULL
+        assert f(1, 4000, 8, A, A, A, None) == BLOCK
+        assert f(1, 4096, 0, A, A, A, None) == DIM
+        assert f(1, 4096, 8, A + 8, A, A, None) == ALIGN
+    assert q4.lib().q4k_gemv(2, 4096, 8, A, A, A, None) == DIM
+
+
+def test_weight_quantizer_validation():
+    f = q4.lib().q4_quantize_weights
+    assert f(8, 128, 32, 0, 8, 0, A, A, A, None, None) == FORMAT
+    assert f(8, 128, 32, 0, 4, 3, A, A, A, None, None) == FORMAT
+    assert f(8, 128, 64, 1, 4, 1, A, A, A, None, None) == NULL
+    assert f(8, 100, 32, 0, 4, 0, A, A, A, None, None) == BLOCK
+    assert f(8, 128, 32, 0, 4, 0, A, A + 4, A, None, None) == ALIGN
+    g = q4.lib().q4k_quantize_weights
+    assert g(8, 300, A, A, None) == BLOCK
+    assert g(8, 256, A, A + 16 + 8, None) == ALIGN
+
+
+def test_binding_raises_with_message():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check")
+    with pytest.raises(ValueError):
+        q4.quantize_act(torch.zeros(2, 64), 32)   # host tensor: refused before any call

@@ -1,0 +1,341 @@
+"""GPU parity: the HIP kernels through the C ABI against the C oracle.
+
+Integer artefacts (activation codes, scales as bit patterns, code sums,
+per-block int32 partials, quantized weight bytes) must be identical; float32
+outputs must be within 1e-5 relative RMS of the oracle. Shapes cover the five
+workloads of the pages at full size (sampled outputs where the oracle would be
+too slow element by element) and ragged sizes spanning several tiles with
+tails in M, N and K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_bit_amd as q4
+import oracle
+import synth
+from tests._gpu import TOL, rel_rms, sample_pairs, to_dev, to_np, workload_data
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"q4_0": oracle.FMT_Q4_0, "affine": oracle.FMT_AFFINE}
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _wts_dev(fmt, wts):
+    if fmt == "q4_0":
+        wq, wd = wts
+        return to_dev(wq), to_dev(wd, torch.float16), None
+    wq, ws, wb = wts
+    return to_dev(wq), to_dev(ws, torch.bfloat16), to_dev(wb, torch.bfloat16)
+
+
+def _oracle_y(fmt, wts, act, K, N, bs, rows=None):
+    wq, ws = wts[0], wts[1]
+    wb = wts[2] if fmt == "affine" else None
+    xq, xs, xsum = act
+    if rows is not None:
+        xq, xs, xsum = xq[rows], xs[rows], xsum[rows]
+    return oracle.q4_gemm(wq, ws, wb, xq, xs, xsum, K, N, bs, FMT[fmt])
+
+
+def _oracle_y_sample(fmt, wts, act, K, N, bs, ms, ns):
+    wq, ws = wts[0], wts[1]
+    wb = wts[2] if fmt == "affine" else None
+    return oracle.q4_gemm_sample(wq, ws, wb, *act, K, N, bs, FMT[fmt], ms, ns)
+
+
+# ---------------------------------------------------------------- activations
+
+ALL = ["q4_0_minilm_64x384x1536", "q4_0_decode_4096", "affine_g64_1024x4096x4096",
+       "affine_g128_4096x4096x14336", "affine_g128_4096x14336x4096"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_quantize_act_bit_exact_workloads(name):
+    print(f"case quantize_act {name}", flush=True)
+    wl, x, _, act, _ = workload_data(name)
+    gx = to_dev(x)
+    gq, gs, gsum = q4.quantize_act(gx, wl.bs)
+    _sync()
+    assert np.array_equal(to_np(gq), act[0])
+    assert np.array_equal(to_np(gs).view(np.uint32), act[1].view(np.uint32))
+    assert np.array_equal(to_np(gsum), act[2])
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_act_edge_cases(bs, dtype):
+    print(f"case quantize_act edges bs={bs} {dtype}", flush=True)
+    rng = np.random.default_rng(bs)
+    M, K = 7, 3 * 128
+    x = (rng.standard_normal((M, K)) * 10.0 ** rng.integers(-6, 6, (M, 1))).astype(np.float32)
+    x[0] = 0.0                                   # all-zero row: xs = 0, codes 0
+    x[1, :bs] = 127.0 * np.sign(rng.standard_normal(bs))
+    x[1, 1:6] = [0.5, 1.5, 2.5, -2.5, 126.5]      # ties: round half to even
+    x[2, 5] = 1e30                               # one huge entry per block
+    x[3] = -x[3]
+    if dtype == "bf16":
+        xin = synth.bf16_bits(x)
+        gx = to_dev(xin)
+    else:
+        xin = x
+        gx = to_dev(x)
+    ref = oracle.quantize_act(xin, bs)
+    got = q4.quantize_act(gx, bs)
+    _sync()
+    assert np.array_equal(to_np(got[0]), ref[0])
+    assert np.array_equal(to_np(got[1]).view(np.uint32), ref[1].view(np.uint32))
+    assert np.array_equal(to_np(got[2]), ref[2])
+
+
+# ---------------------------------------------------------------- weight quantizers
+
+@pytest.mark.parametrize("name", ["q4_0_minilm_64x384x1536", "q4_0_decode_4096", "affine_g64_1024x4096x4096",
+                                  "affine_g128_4096x14336x4096"])
+def test_quantize_weights_bit_exact(name):
+    print(f"case quantize_weights {name}", flush=True)
+    wl, _, w, _, wts = workload_data(name)
+    gw = to_dev(w)
+    got = q4.quantize_weights(gw, wl.fmt, wl.bs)
+    _sync()
+    assert np.array_equal(to_np(got[0]), wts[0])
+    assert np.array_equal(to_np(got[1]), wts[1])
+    if wl.fmt == "affine":
+        assert np.array_equal(to_np(got[2]), wts[2])
+
+
+def test_quantize_weights_edge_blocks():
+    print("case quantize_weights edges", flush=True)
+    rng = np.random.default_rng(3)
+    w = (0.02 * rng.standard_normal((5, 256))).astype(np.float32)
+    w[0, :32] = 0.0                          # zero block: d = -0, codes 8
+    w[1, :32] = 0.01                         # constant block
+    w[2, :32] = w[2, :32] * 0 + np.float32(-0.5)
+    w[2, 7] = 0.5                            # tie of |extremes|: first index wins
+    w[3, 32:64] = 1e-7                       # fp16 subnormal scale
+    ref = oracle.quantize_q4_0(w)
+    got = q4.quantize_weights(to_dev(w), "q4_0", 32)
+    _sync()
+    assert np.array_equal(to_np(got[0]), ref[0]) and np.array_equal(to_np(got[1]), ref[1])
+    wb = synth.bf16_bits(w)
+    for g in (64, 128):
+        ref = oracle.quantize_affine(wb, g)
+        got = q4.quantize_weights(to_dev(wb), "affine", g)
+        _sync()
+        for a, b in zip(got, ref):
+            assert np.array_equal(to_np(a), b)
+
+
+def test_q4k_quantize_weights_bit_exact():
+    print("case q4k quantize_weights", flush=True)
+    wl, _, w, _, blocks = workload_data("q4_k_gemv_1x4096x14336")
+    got = q4.q4k_quantize_weights(to_dev(w))
+    _sync()
+    assert np.array_equal(to_np(got), blocks)
+    rng = np.random.default_rng(4)
+    e = (0.02 * rng.standard_normal((3, 512))).astype(np.float32)
+    e[0, :256] = 0.0
+    e[1, :32] = np.abs(e[1, :32])            # sub-block with min >= 0
+    e[2, 256:] = -np.abs(e[2, 256:])         # all-negative super-block
+    got = q4.q4k_quantize_weights(to_dev(e))
+    _sync()
+    assert np.array_equal(to_np(got), oracle.quantize_q4k(e))
+
+
+# ---------------------------------------------------------------- integer partials
+
+def _partials_case(fmt, bs, M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if fmt == "q4_0":
+        wts = oracle.quantize_q4_0((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    else:
+        wts = oracle.quantize_affine(synth.bf16_bits((0.02 * rng.standard_normal((N, K))).astype(np.float32)), bs)
+    act = oracle.quantize_act(x, bs)
+    return wts, act
+
+
+@pytest.mark.parametrize("fmt,bs,M,K,N", [
+    ("q4_0", 32, 1, 32, 1), ("q4_0", 32, 3, 96, 33), ("q4_0", 32, 65, 160, 31), ("q4_0", 32, 130, 384, 129),
+    ("q4_0", 32, 129, 4096, 257), ("affine", 64, 1, 64, 1), ("affine", 64, 5, 192, 65),
+    ("affine", 64, 131, 320, 130), ("affine", 128, 2, 128, 1537), ("affine", 128, 67, 384, 63),
+    ("affine", 128, 128, 1152, 256),
+])
+def test_gemm_partials_bit_exact_ragged(fmt, bs, M, K, N):
+    print(f"case gemm partials {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, M, K, N, M * 7 + K + N)
+    ref = oracle.q4_partials(wts[0], act[0], K, N, bs, FMT[fmt])
+    got = q4.debug_partials("gemm", fmt, bs, to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]))
+    _sync()
+    assert np.array_equal(to_np(got), ref)
+    if M > 2:
+        sub = q4.debug_partials("gemm", fmt, bs, to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]), 1, M - 1)
+        _sync()
+        assert np.array_equal(to_np(sub), ref[1:M - 1])
+
+
+@pytest.mark.parametrize("fmt,bs,K,N", [("q4_0", 32, 32, 1), ("q4_0", 32, 4096, 4096), ("q4_0", 32, 8224, 37),
+                                        ("affine", 64, 4096, 100), ("affine", 128, 4096, 65),
+                                        ("affine", 128, 14336, 33)])
+def test_gemv_partials_equal_gemm_partials(fmt, bs, K, N):
+    # tract PR #2432: the lane-mapped GEMM kernel is bit-exact with the GEMV path
+    print(f"case gemv/gemm partials {fmt} bs={bs} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, 1, K, N, K + N)
+    ref = oracle.q4_partials(wts[0], act[0], K, N, bs, FMT[fmt])
+    args = (to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]))
+    pv = q4.debug_partials("gemv", fmt, bs, *args)
+    pm = q4.debug_partials("gemm", fmt, bs, *args)
+    _sync()
+    assert np.array_equal(to_np(pv), ref)
+    assert np.array_equal(to_np(pm), ref)
+
+
+@pytest.mark.parametrize("name,rows", [("q4_0_minilm_64x384x1536", None), ("q4_0_decode_4096", None),
+                                       ("affine_g64_1024x4096x4096", (0, 3)),
+                                       ("affine_g64_1024x4096x4096", (1021, 1024)),
+                                       ("affine_g128_4096x4096x14336", (4094, 4096)),
+                                       ("affine_g128_4096x14336x4096", (0, 2))])
+def test_partials_workloads(name, rows):
+    print(f"case partials {name} rows={rows}", flush=True)
+    wl, _, _, act, wts = workload_data(name)
+    m0, m1 = rows if rows else (0, wl.M)
+    ref = oracle.q4_partials(wts[0], act[0], wl.K, wl.N, wl.bs, FMT[wl.fmt], m0, m1)
+    got = q4.debug_partials("gemm", wl.fmt, wl.bs, to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]), m0, m1)
+    _sync()
+    assert np.array_equal(to_np(got), ref)
+    if wl.M == 1:
+        gv = q4.debug_partials("gemv", wl.fmt, wl.bs, to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]))
+        _sync()
+        assert np.array_equal(to_np(gv), ref)
+
+
+# ---------------------------------------------------------------- float outputs
+
+def test_gemv_decode_workload():
+    print("case gemv q4_0 decode 1x4096x4096", flush=True)
+    wl, _, _, act, wts = workload_data("q4_0_decode_4096")
+    g = _wts_dev("q4_0", wts)
+    y = q4.gemv("q4_0", 32, *g, *[to_dev(a) for a in act])
+    _sync()
+    ref = _oracle_y("q4_0", wts, act, wl.K, wl.N, 32)
+    assert rel_rms(to_np(y), ref) <= TOL
+
+
+@pytest.mark.parametrize("fmt,bs,K,N", [("q4_0", 32, 32, 1), ("q4_0", 32, 96, 129), ("q4_0", 32, 8224, 65),
+                                        ("affine", 64, 64, 3), ("affine", 64, 4096, 4096),
+                                        ("affine", 128, 14336, 257)])
+def test_gemv_ragged(fmt, bs, K, N):
+    print(f"case gemv {fmt} bs={bs} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, 1, K, N, 3 * K + N)
+    y = q4.gemv(fmt, bs, *_wts_dev(fmt, wts), *[to_dev(a) for a in act])
+    _sync()
+    assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+
+
+@pytest.mark.parametrize("fmt,bs,M,K,N", [
+    ("q4_0", 32, 1, 32, 1), ("q4_0", 32, 3, 96, 33), ("q4_0", 32, 65, 160, 1537), ("q4_0", 32, 257, 416, 130),
+    ("affine", 64, 1, 64, 5), ("affine", 64, 129, 320, 255), ("affine", 128, 200, 384, 131),
+    ("affine", 128, 64, 4224, 64),
+])
+def test_gemm_ragged(fmt, bs, M, K, N):
+    print(f"case gemm {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, M, K, N, 5 * M + K + N)
+    y = q4.gemm(fmt, bs, *_wts_dev(fmt, wts), *[to_dev(a) for a in act])
+    _sync()
+    assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+
+
+def test_gemm_minilm_workload_full():
+    print("case gemm q4_0 64x384x1536", flush=True)
+    wl, _, _, act, wts = workload_data("q4_0_minilm_64x384x1536")
+    y = q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act])
+    _sync()
+    assert rel_rms(to_np(y), _oracle_y("q4_0", wts, act, wl.K, wl.N, 32)) <= TOL
+
+
+@pytest.mark.parametrize("name", ["affine_g64_1024x4096x4096", "affine_g128_4096x4096x14336",
+                                  "affine_g128_4096x14336x4096"])
+def test_gemm_large_workloads_sampled(name):
+    print(f"case gemm sampled {name}", flush=True)
+    wl, x, _, _, wts = workload_data(name)
+    gx = to_dev(x)
+    gq, gs, gsum = q4.quantize_act(gx, wl.bs)        # the path as timed: quantize, then GEMM
+    y = q4.gemm(wl.fmt, wl.bs, *_wts_dev(wl.fmt, wts), gq, gs, gsum)
+    _sync()
+    act = (to_np(gq), to_np(gs), to_np(gsum))
+    ms, ns = sample_pairs(wl.M, wl.N, 2000, wl.K + wl.N)
+    ref = _oracle_y_sample(wl.fmt, wts, act, wl.K, wl.N, wl.bs, ms, ns)
+    yh = to_np(y)
+    assert rel_rms(yh[ms, ns], ref) <= TOL
+    # whole rows at the tile edges against the oracle as well
+    rows = np.array([0, 127, 128, wl.M - 1])
+    ref_rows = _oracle_y(wl.fmt, wts, act, wl.K, wl.N, wl.bs, rows=rows)
+    assert rel_rms(yh[rows], ref_rows) <= TOL
+
+
+def test_gemm_deterministic():
+    print("case gemm determinism", flush=True)
+    wl, _, _, act, wts = workload_data("affine_g64_1024x4096x4096")
+    g = _wts_dev("affine", wts)
+    a = [to_dev(v) for v in act]
+    y1 = q4.gemm("affine", 64, *g, *a)
+    y2 = q4.gemm("affine", 64, *g, *a)
+    _sync()
+    assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------- Q4_K
+
+def test_q4k_gemv_workload():
+    print("case q4k gemv 1x4096x14336", flush=True)
+    wl, x, _, _, blocks = workload_data("q4_k_gemv_1x4096x14336")
+    y = q4.q4k_gemv(to_dev(blocks), to_dev(x), wl.N)
+    _sync()
+    ms, ns = sample_pairs(1, wl.N, 3000, 11)
+    ref = oracle.q4k_gemm_sample(blocks, x, wl.K, wl.N, ms, ns)
+    assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
+
+
+def test_q4k_gemm_workload():
+    print("case q4k gemm 16x4096x14336", flush=True)
+    wl = synth.workload("q4_k_gemm_16x4096x14336")
+    _, _, _, _, blocks = workload_data("q4_k_gemv_1x4096x14336")   # one weight set for both
+    x = synth.gen.activations(wl)
+    y = q4.q4k_gemm(to_dev(blocks), to_dev(x), wl.N)
+    _sync()
+    ms, ns = sample_pairs(16, wl.N, 3000, 12)
+    ref = oracle.q4k_gemm_sample(blocks, x, wl.K, wl.N, ms, ns)
+    assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (1, 768, 70), (1, 12288, 33), (1, 20480, 5), (3, 512, 63),
+                                   (16, 256, 64), (17, 1024, 65), (40, 2048, 130)])
+def test_q4k_ragged(M, K, N):
+    print(f"case q4k M={M} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(M + K + N)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    blocks = oracle.quantize_q4k(w)
+    ref = oracle.q4k_gemm(blocks, x, K, N)
+    gb, gx = to_dev(blocks), to_dev(x)
+    y = q4.q4k_gemm(gb, gx, N)
+    _sync()
+    assert rel_rms(to_np(y), ref) <= TOL
+    if M == 1:
+        yv = q4.q4k_gemv(gb, gx, N)
+        _sync()
+        assert rel_rms(to_np(yv), ref) <= TOL
+
+
+# ---------------------------------------------------------------- guard
+
+def test_bit_width_guard_on_device():
+    print("case bit-width guard", flush=True)
+    wts, act = _partials_case("q4_0", 32, 1, 64, 4, 1)
+    with pytest.raises(q4.Q4Error) as e:
+        q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act], bits=8)
+    assert e.value.status == 4
