@@ -21,7 +21,7 @@ Q4_FMT_Q4_0, Q4_FMT_AFFINE = 0, 1
 Q4_PATH_GEMV, Q4_PATH_GEMM = 0, 1
 Q4K_BLOCK_BYTES = 144
 
-EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
+EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
            "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string")
 
 
@@ -47,6 +47,7 @@ def lib() -> ctypes.CDLL:
         L.q4_quantize_act.argtypes = [I, I, I, I, P, P, P, P, P]
         L.q4_gemv.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
         L.q4_gemm.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P]
+        L.q4_gemv_fused.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         L.q4_debug_partials.argtypes = [I, I, I, I, I, I, I, P, P, P, I, I, P, P]
         L.q4k_gemv.argtypes = [I, I, I, P, P, P, P]
         L.q4k_gemm.argtypes = [I, I, I, P, P, P, P]
@@ -132,6 +133,22 @@ def gemv(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int =
     if y is None:
         y = torch.empty((xq.shape[0], wq.shape[0]), dtype=torch.float32, device=wq.device)
     return _matmul("q4_gemv", xq.shape[0], fmt, bs, wq, wscale, wbias, xq, xs, xsum, y, bits, stream)
+
+
+def gemv_fused(fmt: str, bs: int, x, wq, wscale, wbias, y=None, act_out=None, bits: int = 4, stream=None):
+    """Fused decode step: quantize x [1][K] and run the GEMV in one launch -> y float32 [1][N].
+    act_out = (xq, xs, xsum) receives the activation codes the kernel used."""
+    N, Kh = wq.shape
+    K = 2 * Kh
+    if x.shape[1] != K:
+        raise ValueError("x and wq disagree on K")
+    if y is None:
+        y = torch.empty((x.shape[0], N), dtype=torch.float32, device=wq.device)
+    xq, xs, xsum = act_out if act_out is not None else (None, None, None)
+    _check(lib().q4_gemv_fused(x.shape[0], K, N, bs, _fmt(fmt), bits, _xdtype(x), _ptr(x), _ptr(wq), _ptr(wscale),
+                               _ptr(wbias), _ptr(y), _ptr(xq), _ptr(xs), _ptr(xsum), _stream(stream)),
+           "q4_gemv_fused")
+    return y
 
 
 def gemm(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int = 4, stream=None):

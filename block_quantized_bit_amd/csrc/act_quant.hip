@@ -6,7 +6,8 @@
 // their maxima and code sums with lane exchanges. Loads are 16 bytes per
 // thread (bf16) or 2 x 16 bytes (f32); the 8 codes are written with one
 // 8-byte store. The block scale is amax / 127 in correctly rounded float32 and
-// every code is round-half-even of a correctly rounded float32 quotient.
+// every code is round-half-even of a correctly rounded float32 quotient
+// (act_code: a reciprocal multiply, with the exact quotient near ties).
 #include "common.h"
 #include "kernels.h"
 
@@ -43,15 +44,13 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(long long nthreads, c
     for (int off = 1; off < L; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
 
     const float s = amax / 127.0f;  // correctly rounded float32 division
+    const float inv = act_inverse(s);
     int q[8];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        int c = 0;
-        if (amax != 0.0f) {
-            c = (int)rintf(v[i] / s);  // round half to even of the float32 quotient
-            c = min(127, max(-127, c));
-        }
+        // round half to even of the correctly rounded float32 quotient v / s
+        const int c = (amax != 0.0f) ? act_code(v[i], s, inv) : 0;
         q[i] = c;
         sum += c;
     }

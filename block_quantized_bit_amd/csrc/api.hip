@@ -32,6 +32,8 @@ int matmul_status(int M, int K, int N, int bs, int fmt, int bits) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
 
+constexpr int Q4_GEMV_MAX_K = 32768;  // activation codes staged in LDS
+
 }  // namespace
 
 extern "C" {
@@ -75,11 +77,28 @@ int q4_gemv(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, c
             const int8_t* xq, const float* xs, const int32_t* xsum, float* y, void* stream) {
     int st = matmul_status(M, K, N, bs, fmt, bits);
     if (st) return st;
-    if (M != 1) return Q4_ERR_DIM;
+    if (M != 1 || K > Q4_GEMV_MAX_K) return Q4_ERR_DIM;
     st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
     if (st) return st;
     return hip_status(q4::launch_gemv(K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
                                       static_cast<hipStream_t>(stream)));
+}
+
+int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, const void* x, const uint8_t* wq,
+                  const void* wscale, const void* wbias, float* y, int8_t* xq_out, float* xs_out, int32_t* xsum_out,
+                  void* stream) {
+    int st = matmul_status(M, K, N, bs, fmt, bits);
+    if (st) return st;
+    if (xdtype != Q4_DT_F32 && xdtype != Q4_DT_BF16) return Q4_ERR_FORMAT;
+    if (M != 1 || K > Q4_GEMV_MAX_K) return Q4_ERR_DIM;
+    if (!x || !wq || !wscale || !y || (fmt == Q4_FMT_AFFINE && !wbias)) return Q4_ERR_NULL;
+    const bool any_out = xq_out || xs_out || xsum_out;
+    if (any_out && !(xq_out && xs_out && xsum_out)) return Q4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(wscale, 2) || (wbias && !aligned(wbias, 2)) ||
+        !aligned(y, 4) || (any_out && (!aligned(xq_out, 16) || !aligned(xs_out, 4) || !aligned(xsum_out, 4))))
+        return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_gemv_fused(K, N, bs, fmt, xdtype == Q4_DT_BF16, x, wq, wscale, wbias, y, xq_out,
+                                            xs_out, xsum_out, static_cast<hipStream_t>(stream)));
 }
 
 int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale, const void* wbias,
@@ -108,6 +127,7 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
     const int32_t* xsum0 = xsum + (size_t)m0 * ng;
     if (path == Q4_PATH_GEMV) {
         if (m1 - m0 != 1) return Q4_ERR_RANGE;
+        if (K > Q4_GEMV_MAX_K) return Q4_ERR_DIM;
         return hip_status(q4::launch_gemv(K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
                                           partials, s));
     }

@@ -69,4 +69,27 @@ __device__ __forceinline__ uint32_t hi_nibbles(uint32_t w) { return (w >> 4) & 0
 // 0x88 (no carry between bytes); flipping bit 7 then subtracts 128.
 __device__ __forceinline__ uint32_t minus8_bytes(uint32_t q) { return (q + 0x78787878u) ^ 0x80808080u; }
 
+// ---- activation codes -----------------------------------------------------------
+
+// Inverse of a block scale for the fast path of act_code, or 0 when the fast
+// path must not be used (scale zero or subnormal).
+__device__ __forceinline__ float act_inverse(float s) {
+    return (s >= 0x1p-125f) ? __builtin_amdgcn_rcpf(s) : 0.0f;
+}
+
+// Code of one activation: clamp(round_half_even(v / s), -127, 127) with the
+// correctly rounded float32 quotient v / s, for |v| <= 127 s (s = amax / 127).
+// Fast path: r = v * rcp(s). v_rcp_f32 is within 1 ulp, so for |v / s| < 128
+// r is within 2^-15 of the rounded quotient; when r is at least 2^-12 away from
+// the nearest half-integer both sit inside the same rounding cell and round to
+// the same integer. Near a half-integer (and when `inv` is 0) the exact
+// quotient decides.
+__device__ __forceinline__ int act_code(float v, float s, float inv) {
+    float r = v * inv;
+    const float f = r - floorf(r);
+    if (inv == 0.0f || fabsf(f - 0.5f) < 0x1p-12f) r = v / s;
+    const int c = (int)rintf(r);
+    return min(127, max(-127, c));
+}
+
 }  // namespace q4

@@ -16,6 +16,12 @@ hipError_t launch_gemv(int K, int N, int bs, int fmt, const uint8_t* wq, const v
                        const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                        hipStream_t stream);
 
+// Decode GEMV that quantizes x itself; the optional *_out pointers receive the
+// activation codes it used (written by one workgroup).
+hipError_t launch_gemv_fused(int K, int N, int bs, int fmt, bool xbf16, const void* x, const uint8_t* wq,
+                             const void* wscale, const void* wbias, float* y, int8_t* xq_out, float* xs_out,
+                             int32_t* xsum_out, hipStream_t stream);
+
 hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
                        const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                        int32_t* partials, hipStream_t stream);

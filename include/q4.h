@@ -101,12 +101,27 @@ int q4_quantize_act(int M, int K, int bs, int xdtype, const void* x,
  * int8 dot-product instruction; one wavefront reduces each output.
  * wq [N][K/2] (16-byte aligned), wscale/wbias as in the format enum,
  * xq [1][K] (16-byte aligned), xs, xsum [1][K/bs] from q4_quantize_act,
- * y [1][N] float32.
+ * y [1][N] float32. K <= 32768 (the activation codes are staged in LDS).
  */
 int q4_gemv(int M, int K, int N, int bs, int fmt, int bits,
             const uint8_t* wq, const void* wscale, const void* wbias,
             const int8_t* xq, const float* xs, const int32_t* xsum,
             float* y, void* stream);
+
+/*
+ * Fused decode step (M must be 1): q4_quantize_act of x followed by q4_gemv,
+ * in one launch. Every workgroup quantizes x into LDS while its weight loads
+ * are in flight (tract PR #2432 measures the per-call activation
+ * re-quantization as overhead of the decode op; here it costs no extra pass
+ * over memory and no extra launch). The codes are bit-identical to those of
+ * q4_quantize_act. x [1][K] float32 or bfloat16 (xdtype), 16-byte aligned.
+ * xq_out [1][K], xs_out, xsum_out [1][K/bs]: either all NULL or all set; when
+ * set they receive the activation codes the kernel used (xq_out 16-byte
+ * aligned). Other arguments as q4_gemv.
+ */
+int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, const void* x,
+                  const uint8_t* wq, const void* wscale, const void* wbias, float* y,
+                  int8_t* xq_out, float* xs_out, int32_t* xsum_out, void* stream);
 
 /*
  * Prefill GEMM, any M >= 1: Y[m][n] as q4_gemv for every row m, computed on

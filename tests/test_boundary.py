@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None
@@ -68,6 +68,24 @@ def test_matmul_validation(entry, kw, status):
 
 def test_gemv_requires_one_row():
     assert q4.lib().q4_gemv(*gemm_args(M=2)) == DIM
+
+
+def test_gemv_fused_validation():
+    f = q4.lib().q4_gemv_fused
+    base = [1, 128, 8, 32, 0, 4, 0, A, A, A, None, A, None, None, None, None]
+    assert f(*base[:5], 8, *base[6:]) == FORMAT             # bits
+    args = list(base); args[6] = 5
+    assert f(*args) == FORMAT                               # x dtype
+    args = list(base); args[0] = 2
+    assert f(*args) == DIM                                  # decode only
+    args = list(base); args[1] = 65536
+    assert f(*args) == DIM                                  # K beyond the LDS staging
+    args = list(base); args[12] = A
+    assert f(*args) == NULL                                 # partial set of code outputs
+    args = list(base); args[7] = A + 4
+    assert f(*args) == ALIGN
+    args = list(base); args[12], args[13], args[14] = A + 8, A, A
+    assert f(*args) == ALIGN
 
 
 def test_quantize_act_validation():

@@ -339,3 +339,82 @@ def test_bit_width_guard_on_device():
     with pytest.raises(q4.Q4Error) as e:
         q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act], bits=8)
     assert e.value.status == 4
+
+
+# ---------------------------------------------------------------- fused decode step
+
+def _near_tie_activations(M, K, bs, seed):
+    """Blocks whose quotients v / xs sit within a few ulps of half-integers:
+    the rounding of each code is decided by the last bits of the division."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((M, K), dtype=np.float32)
+    for m in range(M):
+        for b in range(K // bs):
+            amax = np.float32(rng.uniform(0.5, 2.0) * 10.0 ** rng.integers(-3, 3))
+            s = np.float32(amax / np.float32(127.0))
+            k = rng.integers(-126, 126, bs).astype(np.float64) + 0.5
+            v = (k * np.float64(s)).astype(np.float32)
+            ulps = rng.integers(-3, 4, bs).astype(np.int32)
+            v = (v.view(np.int32) + ulps).view(np.float32)
+            v[0] = amax                      # fixes the block maximum
+            v = np.clip(v, -amax, amax)
+            x[m, b * bs:(b + 1) * bs] = v
+    return x
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+def test_quantize_act_near_ties(bs):
+    print(f"case quantize_act near ties bs={bs}", flush=True)
+    x = _near_tie_activations(16, 4096, bs, bs + 100)
+    ref = oracle.quantize_act(x, bs)
+    got = q4.quantize_act(to_dev(x), bs)
+    _sync()
+    for a, b in zip(got, ref):
+        assert np.array_equal(to_np(a).view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("fmt,bs,xdt", [("q4_0", 32, "f32"), ("q4_0", 32, "bf16"), ("affine", 64, "bf16"),
+                                        ("affine", 128, "f32"), ("affine", 128, "bf16")])
+def test_gemv_fused_decode(fmt, bs, xdt):
+    print(f"case gemv_fused {fmt} bs={bs} x={xdt}", flush=True)
+    if fmt == "q4_0":
+        wl, x, _, _, wts = workload_data("q4_0_decode_4096")
+        if xdt == "bf16":
+            x = synth.bf16_bits(synth.bf16_bits_to_f32(synth.bf16_bits(x)))
+    else:
+        rng = np.random.default_rng(bs)
+        x32 = rng.standard_normal((1, 4096)).astype(np.float32)
+        x = synth.bf16_bits(x32) if xdt == "bf16" else x32
+        wts = oracle.quantize_affine(synth.bf16_bits((0.02 * rng.standard_normal((1000, 4096))).astype(np.float32)),
+                                     bs)
+    K, N = 4096, wts[0].shape[0]
+    act = oracle.quantize_act(x, bs)
+    gx = to_dev(x)
+    out = (torch.empty((1, K), dtype=torch.int8, device=gx.device),
+           torch.empty((1, K // bs), dtype=torch.float32, device=gx.device),
+           torch.empty((1, K // bs), dtype=torch.int32, device=gx.device))
+    y = q4.gemv_fused(fmt, bs, gx, *_wts_dev(fmt, wts), act_out=out)
+    y2 = q4.gemv_fused(fmt, bs, gx, *_wts_dev(fmt, wts))
+    _sync()
+    for a, b in zip(out, act):
+        assert np.array_equal(to_np(a).view(np.uint8), b.view(np.uint8))
+    ref = _oracle_y(fmt, wts, act, K, N, bs)
+    assert rel_rms(to_np(y), ref) <= TOL
+    assert torch.equal(y, y2)
+
+
+def test_gemv_fused_near_ties_and_ragged():
+    print("case gemv_fused near ties, ragged N", flush=True)
+    x = _near_tie_activations(1, 8192, 32, 5)
+    rng = np.random.default_rng(6)
+    wts = oracle.quantize_q4_0((0.02 * rng.standard_normal((77, 8192))).astype(np.float32))
+    act = oracle.quantize_act(x, 32)
+    gx = to_dev(x)
+    out = (torch.empty((1, 8192), dtype=torch.int8, device=gx.device),
+           torch.empty((1, 256), dtype=torch.float32, device=gx.device),
+           torch.empty((1, 256), dtype=torch.int32, device=gx.device))
+    y = q4.gemv_fused("q4_0", 32, gx, *_wts_dev("q4_0", wts), act_out=out)
+    _sync()
+    for a, b in zip(out, act):
+        assert np.array_equal(to_np(a).view(np.uint8), b.view(np.uint8))
+    assert rel_rms(to_np(y), _oracle_y("q4_0", wts, act, 8192, 77, 32)) <= TOL
