@@ -105,7 +105,8 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, c
             const int8_t* xq, const float* xs, const int32_t* xsum, float* y, void* stream) {
     int st = matmul_status(M, K, N, bs, fmt, bits);
     if (st) return st;
-    if (M > (1 << 23)) return Q4_ERR_DIM;  // grid rows of 128
+    // buffer loads address each operand with 32-bit byte offsets
+    if ((long long)M * K >= (1LL << 31) || (long long)N * (K / 2) >= (1LL << 31)) return Q4_ERR_DIM;
     st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
     if (st) return st;
     return hip_status(q4::launch_gemm(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
@@ -120,7 +121,7 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
     if (!wq || !xq || !xsum || !partials) return Q4_ERR_NULL;
     if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(xsum, 4) || !aligned(partials, 4)) return Q4_ERR_ALIGN;
     if (m0 < 0 || m1 > M || m0 >= m1) return Q4_ERR_RANGE;
-    if (m1 - m0 > (1 << 23)) return Q4_ERR_DIM;
+    if ((long long)(m1 - m0) * K >= (1LL << 31) || (long long)N * (K / 2) >= (1LL << 31)) return Q4_ERR_DIM;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int ng = K / bs;
     const int8_t* xq0 = xq + (size_t)m0 * K;

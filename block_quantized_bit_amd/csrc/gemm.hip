@@ -5,18 +5,38 @@
 // MLX PR #4802: with affine weights the int8 x int8 MMA runs on the original
 // codes and the per-group scale and bias are applied inside the kernel.
 //
-// Tiling: a workgroup of 4 wavefronts computes a 128 x 128 tile of Y; each
-// wavefront owns 64 x 64 (2 x 2 tiles of v_mfma_i32_32x32x32_i8). The K loop
-// walks 128-wide stages. Per stage the int8 activation tile and the weight
-// tile are staged through LDS; the weight nibbles are unpacked once, on the
-// way into LDS (to q - 8 as signed bytes for Q4_0, to q for affine), so every
-// MFMA reads ready int8 operands. One 32-wide K step is one Q4_0 block; an
-// affine group of 64 / 128 accumulates 2 / 4 steps in int32. After each block
-// or group the int32 tile is rescaled into float accumulators:
-//   Q4_0:   acc += xs[m] * d[n] * P
-//   affine: acc += xs[m] * (s[n] * A) + (xs * xsum)[m] * b[n]
-// The next stage's global loads are issued into registers before the current
-// stage is computed, so their latency overlaps the matrix work.
+// Tiling: a workgroup of 2 x 2 wavefronts computes a 128 x 128 tile of Y; each
+// wavefront owns 2 x 2 tiles of v_mfma_i32_32x32x32_i8 (32 x 32 outputs; one
+// 32-wide K step is one Q4_0 block). Two workgroups share a CU (registers are
+// held under 256 per lane and LDS under 80 KB per workgroup); they are not
+// synchronised with each other, so one's matrix work overlaps the other's
+// float rescale on every SIMD.
+//
+// K is walked in 128-wide stages through two LDS buffers. The stage's global
+// loads are buffer loads with a per-lane offset fixed for the whole kernel
+// and the stage offset in a scalar register; rows past M or N read as zero
+// (the buffer range check), so the staging needs no masks. After the one
+// barrier of a stage, the registers holding stage s+1 are written to the free
+// buffer (weight nibbles unpacked on the way: q - 8 as signed bytes for Q4_0,
+// q for affine), the loads of stage s+2 are issued, and stage s is computed.
+// LDS rows are 128 bytes with the 16-byte chunk index XORed with bits of the
+// row index, so the MFMA fragment reads (32 rows at one K offset) hit all banks.
+//
+// Per block (Q4_0) or group (affine, 64 / 128 weights = 2 / 4 MFMA steps) the
+// int32 tile is rescaled into float accumulators:
+//   Q4_0:   acc += xs[m] * (d[n] * P)                 3 VALU ops per output
+//   affine: acc += xs[m] * (s[n] * A)                 3 VALU ops per output
+//           acc += sum_g (xs * xsum)[m, g] * b[n, g]  on the f32 matrix core
+// The affine bias term is a rank-(K/g) product, so it runs as
+// v_mfma_f32_32x32x2_f32 with two groups in its two K slots instead of a
+// fourth VALU op per output.
+//
+// Workgroups are mapped to tiles so that the workgroups resident on one XCD
+// (dispatch is round-robin over the 8 XCDs) take neighbouring tiles, grouped
+// GROUP_M row tiles at a time, which keeps their shared A and B panels in
+// that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -24,111 +44,187 @@ namespace q4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, KS = 128;
-constexpr int LDS_STRIDE = KS + 16;  // bytes per LDS row; the pad spreads rows over the banks
+constexpr int BM = 128, BN = 128;    // workgroup tile
+constexpr int KS = 128;              // K per stage
+constexpr int NT = 256;              // threads per workgroup
+constexpr int GROUP_M = 8;           // row tiles per tile group
+constexpr int NXCD = 8;
+constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data format
+
+template <int G, int FMT>
+struct Stage {
+    static constexpr int GPS = KS / G;
+    static constexpr int NB = (FMT == 1) ? GPS : 1;  // affine keeps the bias operands too
+    uint4 a[BM * KS / 16];
+    uint4 b[BN * KS / 16];
+    float xs[GPS][BM];
+    float ws[GPS][BN];
+    float xb[NB][BM];
+    float wb[NB][BN];
+};
+
+// 16-byte chunk c (0..7) of LDS row r. The chunk index is XORed with
+// (r & 7) ^ ((r >> 3) & 1): any 8 consecutive aligned rows use 8 different
+// chunk positions, and any 16 consecutive aligned rows use 16 different
+// 16-byte slots of a 256-byte bank line (even and odd rows fill its two
+// halves), so a 32-row fragment read at one K offset is conflict-free whether
+// the banks serve 8 or 16 lanes of a 128-bit read per cycle.
+__device__ __forceinline__ int swz(int r, int c) { return r * (KS / 16) + (c ^ (r & 7) ^ ((r >> 3) & 1)); }
+
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int total = tiles_m * tiles_n;
+    // consecutive workgroup ids go to different XCDs: give each XCD a contiguous range of tiles
+    int t = bid;
+    if (total % NXCD == 0) t = (bid % NXCD) * (total / NXCD) + bid / NXCD;
+    const int per_group = GROUP_M * tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int r = t - group * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
+}
 
 template <int FMT, int G, bool PARTIALS>
-__global__ __launch_bounds__(256) void gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
-                                                   const uint16_t* __restrict__ wscale,
-                                                   const uint16_t* __restrict__ wbias, const int8_t* __restrict__ xq,
-                                                   const float* __restrict__ xs, const int32_t* __restrict__ xsum,
-                                                   float* __restrict__ y, int32_t* __restrict__ partials) {
+__global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
+                                                      const uint16_t* __restrict__ wscale,
+                                                      const uint16_t* __restrict__ wbias,
+                                                      const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                      const int32_t* __restrict__ xsum, float* __restrict__ y,
+                                                      int32_t* __restrict__ partials) {
     constexpr int GPS = KS / G;  // blocks or groups per stage
-    constexpr int SPG = G / 32;  // 32-wide MFMA steps per block or group
+    constexpr int SPG = G / 32;  // MFMA K steps per block or group
+    constexpr int A_CH = BM * (KS / 16) / NT;  // 16-byte activation chunks per thread per stage (4)
+    constexpr int B_CH = BN * (KS / 32) / NT;  // 16-byte packed weight chunks per thread per stage (2)
+    constexpr bool AFF = FMT == 1;
+    constexpr bool BIAS_MFMA = AFF && !PARTIALS;
+    static_assert(A_CH * NT == BM * (KS / 16) && B_CH * NT == BN * (KS / 32), "tile / thread mismatch");
 
-    __shared__ __attribute__((aligned(16))) int8_t As[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) int8_t Bs[BN * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) float xs_s[GPS][BM];
-    __shared__ __attribute__((aligned(16))) float xb_s[GPS][BM];
-    __shared__ float ws_s[GPS][BN];
-    __shared__ float wb_s[GPS][BN];
+    using St = Stage<G, FMT>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    St* stage_buf = reinterpret_cast<St*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    int tm, tn;
+    tile_of(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
     const int ngroups = K / G;
     const int nstages = (K + KS - 1) / KS;
-    const size_t wrow = (size_t)(K >> 1);
+    const int half = lane >> 5, l32 = lane & 31;
 
-    uint4 ra[4], rb[2];
-    float rxs[2], rxb[2], rws[2], rwb[2];
+    // ---------------------------------------------------------------- staging
+    const __amdgpu_buffer_rsrc_t r_a = rsrc(xq, (uint32_t)((size_t)M * K));
+    const __amdgpu_buffer_rsrc_t r_b = rsrc(wq, (uint32_t)((size_t)N * (K / 2)));
+    const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
+    const __amdgpu_buffer_rsrc_t r_xsum = rsrc(xsum, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
+    const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, PARTIALS ? 0u : (uint32_t)((size_t)N * ngroups * 2));
+    const __amdgpu_buffer_rsrc_t r_wb =
+        rsrc(wbias, (PARTIALS || !AFF) ? 0u : (uint32_t)((size_t)N * ngroups * 2));
+    constexpr uint32_t OUT = 0x80000000u;  // beyond every buffer range: reads as zero
 
+    // per-lane offsets, fixed for the whole kernel (each stage adds a scalar offset)
+    uint32_t off_a[A_CH], off_b[B_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+        const int idx = tid + NT * i, r = idx >> 3, c16 = idx & 7;
+        off_a[i] = (m0 + r < M) ? (uint32_t)((m0 + r) * K + c16 * 16) : OUT;
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+        const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
+        off_b[i] = (n0 + c < N) ? (uint32_t)((n0 + c) * (K / 2) + b * 16) : OUT;
+    }
+    // scale staging: the thread covers (gi, r) = divmod(tid + NT*i, BM), GPS*BM values
+    constexpr int SC_N = (GPS * BM + NT - 1) / NT;
+    uint32_t off_xs[SC_N], off_ws[SC_N];
+#pragma unroll
+    for (int i = 0; i < SC_N; ++i) {
+        const int idx = tid + NT * i, gi = idx / BM, r = idx % BM;
+        const bool used = idx < GPS * BM;
+        off_xs[i] = (used && m0 + r < M) ? (uint32_t)(((m0 + r) * ngroups + gi) * 4) : OUT;
+        off_ws[i] = (used && n0 + r < N) ? (uint32_t)(((n0 + r) * ngroups + gi) * 2) : OUT;
+    }
+
+    uint4 ra[A_CH], rb[B_CH];
+    float rxs[SC_N];
+    int32_t rxsum[SC_N];
+    uint32_t rws[SC_N], rwb[SC_N];
+
+    // Every load that is not needed (rows past M or N, K past the end of the
+    // row in the last stage) gets an out-of-range lane offset, so it reads zero
+    // without touching memory whether or not the range check counts the
+    // scalar offset.
     auto load_stage = [&](int st) {
         const int k0 = st * KS;
         const int ks = min(KS, K - k0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, r = idx >> 3, c16 = idx & 7;
-            const int m = m0 + r;
-            ra[i] = (m < M && c16 * 16 < ks) ? *reinterpret_cast<const uint4*>(xq + (size_t)m * K + k0 + c16 * 16)
-                                             : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < A_CH; ++i) {
+            const int c16 = (tid + NT * i) & 7;
+            const uint32_t o = (c16 * 16 < ks) ? off_a[i] : OUT;
+            ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_a, o, k0, 0));
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, c = idx >> 2, b = idx & 3;
-            const int n = n0 + c;
-            const uint32_t pad = (FMT == 0) ? 0x88888888u : 0u;  // codes of a zero weight
-            rb[i] = (n < N && b * 32 < ks)
-                        ? *reinterpret_cast<const uint4*>(wq + (size_t)n * wrow + (size_t)((k0 >> 5) + b) * 16)
-                        : make_uint4(pad, pad, pad, pad);
+        for (int i = 0; i < B_CH; ++i) {
+            const int b = (tid + NT * i) & 3;
+            const uint32_t o = (b * 32 < ks) ? off_b[i] : OUT;
+            rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_b, o, k0 >> 1, 0));
         }
+        if (!PARTIALS) {
+            const int g0 = k0 / G;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i;
-            rxs[i] = rxb[i] = rws[i] = rwb[i] = 0.0f;
-            if (idx < GPS * 128) {
-                const int gi = idx >> 7, r = idx & 127;
-                const int g = k0 / G + gi;
-                if (gi * G < ks) {
-                    const int m = m0 + r, n = n0 + r;
-                    if (!PARTIALS && m < M) {
-                        rxs[i] = xs[(size_t)m * ngroups + g];
-                        if (FMT == 1) rxb[i] = rxs[i] * (float)xsum[(size_t)m * ngroups + g];
-                    }
-                    if (!PARTIALS && n < N) {
-                        if (FMT == 0) {
-                            rws[i] = half_to_float(wscale[(size_t)n * ngroups + g]);
-                        } else {
-                            rws[i] = bf16_to_float(wscale[(size_t)n * ngroups + g]);
-                            rwb[i] = bf16_to_float(wbias[(size_t)n * ngroups + g]);
-                        }
-                    }
-                }
+            for (int i = 0; i < SC_N; ++i) {
+                const int gi = (tid + NT * i) / BM;
+                const bool in = gi * G < ks;
+                const uint32_t ox = in ? off_xs[i] : OUT, ow = in ? off_ws[i] : OUT;
+                rxs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, ox, g0 * 4, 0));
+                if (AFF) rxsum[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r_xsum, ox, g0 * 4, 0);
+                rws[i] = __builtin_amdgcn_raw_buffer_load_b16(r_ws, ow, g0 * 2, 0);
+                if (AFF) rwb[i] = __builtin_amdgcn_raw_buffer_load_b16(r_wb, ow, g0 * 2, 0);
             }
         }
     };
 
-    auto store_stage = [&]() {
+    auto store_stage = [&](St& S) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + 256 * i, r = idx >> 3, c16 = idx & 7;
-            *reinterpret_cast<uint4*>(&As[r * LDS_STRIDE + c16 * 16]) = ra[i];
+        for (int i = 0; i < A_CH; ++i) {
+            const int idx = tid + NT * i, r = idx >> 3, c16 = idx & 7;
+            S.a[swz(r, c16)] = ra[i];
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, c = idx >> 2, b = idx & 3;
+        for (int i = 0; i < B_CH; ++i) {
+            const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
             uint4 lo = make_uint4(lo_nibbles(rb[i].x), lo_nibbles(rb[i].y), lo_nibbles(rb[i].z), lo_nibbles(rb[i].w));
             uint4 hi = make_uint4(hi_nibbles(rb[i].x), hi_nibbles(rb[i].y), hi_nibbles(rb[i].z), hi_nibbles(rb[i].w));
             if (FMT == 0) {
                 lo = make_uint4(minus8_bytes(lo.x), minus8_bytes(lo.y), minus8_bytes(lo.z), minus8_bytes(lo.w));
                 hi = make_uint4(minus8_bytes(hi.x), minus8_bytes(hi.y), minus8_bytes(hi.z), minus8_bytes(hi.w));
             }
-            *reinterpret_cast<uint4*>(&Bs[c * LDS_STRIDE + b * 32]) = lo;
-            *reinterpret_cast<uint4*>(&Bs[c * LDS_STRIDE + b * 32 + 16]) = hi;
+            S.b[swz(c, 2 * b)] = lo;      // k = 32b .. 32b+15
+            S.b[swz(c, 2 * b + 1)] = hi;  // k = 32b+16 .. 32b+31
         }
+        if (!PARTIALS) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < GPS * 128) {
-                const int gi = idx >> 7, r = idx & 127;
-                xs_s[gi][r] = rxs[i];
-                xb_s[gi][r] = rxb[i];
-                ws_s[gi][r] = rws[i];
-                wb_s[gi][r] = rwb[i];
+            for (int i = 0; i < SC_N; ++i) {
+                const int idx = tid + NT * i;
+                if (idx < GPS * BM) {
+                    const int gi = idx / BM, r = idx % BM;
+                    S.xs[gi][r] = rxs[i];
+                    S.ws[gi][r] = AFF ? bf16_to_float(rws[i]) : half_to_float(rws[i]);
+                    if (AFF) {
+                        S.xb[gi][r] = rxs[i] * (float)rxsum[i];
+                        S.wb[gi][r] = bf16_to_float(rwb[i]);
+                    }
+                }
             }
         }
     };
 
+    // ---------------------------------------------------------------- compute
     v16f acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -137,16 +233,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int K, int N, const ui
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    const int half = lane >> 5, l32 = lane & 31;
     const int arow0 = wm * 64 + l32, brow0 = wn * 64 + l32;
+    float bva[2] = {0.0f, 0.0f}, bvb[2] = {0.0f, 0.0f};  // bias operands of a pending slot-0 group
+    bool bias_pending = false;
 
-    load_stage(0);
-    for (int st = 0; st < nstages; ++st) {
+    auto do_stage = [&](int st, auto par) {
+        constexpr int P = decltype(par)::value;
         __syncthreads();
-        store_stage();
-        __syncthreads();
-        if (st + 1 < nstages) load_stage(st + 1);
-
+        if (st + 1 < nstages) store_stage(stage_buf[P ^ 1]);
+        if (st + 2 < nstages) load_stage(st + 2);
+        const St& S = stage_buf[P];
         const int k0 = st * KS;
         const int ks = min(KS, K - k0);
 #pragma unroll
@@ -155,84 +251,112 @@ __global__ __launch_bounds__(256) void gemm_kernel(int M, int K, int N, const ui
             v16i pi[2][2];
 #pragma unroll
             for (int s = 0; s < SPG; ++s) {
-                const int kk = gi * G + s * 32 + 16 * half;
-                v4i a0 = *reinterpret_cast<const v4i*>(&As[arow0 * LDS_STRIDE + kk]);
-                v4i a1 = *reinterpret_cast<const v4i*>(&As[(arow0 + 32) * LDS_STRIDE + kk]);
-                v4i b0 = *reinterpret_cast<const v4i*>(&Bs[brow0 * LDS_STRIDE + kk]);
-                v4i b1 = *reinterpret_cast<const v4i*>(&Bs[(brow0 + 32) * LDS_STRIDE + kk]);
-                if (s == 0) {
-                    const v16i z = {};
-                    pi[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, z, 0, 0, 0);
-                    pi[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b1, z, 0, 0, 0);
-                    pi[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, z, 0, 0, 0);
-                    pi[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1, z, 0, 0, 0);
-                } else {
-                    pi[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b0, pi[0][0], 0, 0, 0);
-                    pi[0][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a0, b1, pi[0][1], 0, 0, 0);
-                    pi[1][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b0, pi[1][0], 0, 0, 0);
-                    pi[1][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a1, b1, pi[1][1], 0, 0, 0);
-                }
+                const int chunk = gi * (G / 16) + 2 * s + half;
+                v4i af[2], bf[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) af[i] = __builtin_bit_cast(v4i, S.a[swz(arow0 + 32 * i, chunk)]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bf[j] = __builtin_bit_cast(v4i, S.b[swz(brow0 + 32 * j, chunk)]);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (s == 0) {
+                            const v16i z = {};
+                            pi[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], z, 0, 0, 0);
+                        } else {
+                            pi[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], pi[i][j], 0, 0, 0);
+                        }
+                    }
             }
-            // D layout of the 32x32 MFMA: lane holds column l32, rows
-            // 8*(r/4) + 4*half + r%4 for r = 0..15.
+            // D layout of the 32x32 MFMA: lane holds column l32, rows 8*(r/4) + 4*half + r%4.
             if (PARTIALS) {
                 const int g = k0 / G + gi;
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        const int n = n0 + wn * 64 + nt * 32 + l32;
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = n0 + wn * 64 + 32 * j + l32;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                            if (m < M && n < N) partials[((size_t)m * N + n) * ngroups + g] = pi[mt][nt][r];
+                            const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                            if (m < M && n < N) partials[((size_t)m * N + n) * ngroups + g] = pi[i][j][r];
                         }
                     }
-            } else {
-                float wsv[2], wbv[2];
+                continue;
+            }
+            float wsv[2];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    wsv[nt] = ws_s[gi][wn * 64 + nt * 32 + l32];
-                    wbv[nt] = wb_s[gi][wn * 64 + nt * 32 + l32];
+            for (int j = 0; j < 2; ++j) wsv[j] = S.ws[gi][wn * 64 + 32 * j + l32];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                float xsv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(&S.xs[gi][wm * 64 + 32 * i + 8 * q + 4 * half]);
+                    xsv[4 * q] = v.x; xsv[4 * q + 1] = v.y; xsv[4 * q + 2] = v.z; xsv[4 * q + 3] = v.w;
                 }
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    float xsv[16], xbv[16];
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int r0 = wm * 64 + mt * 32 + 8 * j + 4 * half;
-                        const float4 v = *reinterpret_cast<const float4*>(&xs_s[gi][r0]);
-                        xsv[4 * j] = v.x; xsv[4 * j + 1] = v.y; xsv[4 * j + 2] = v.z; xsv[4 * j + 3] = v.w;
-                        if (FMT == 1) {
-                            const float4 u = *reinterpret_cast<const float4*>(&xb_s[gi][r0]);
-                            xbv[4 * j] = u.x; xbv[4 * j + 1] = u.y; xbv[4 * j + 2] = u.z; xbv[4 * j + 3] = u.w;
-                        }
-                    }
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] += xsv[r] * (wsv[j] * (float)pi[i][j][r]);
+            }
+            if (BIAS_MFMA) {
+                // two groups per f32 MFMA: lanes of half h supply group slot h
+                float va[2], vb[2];
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt)
+                for (int i = 0; i < 2; ++i) va[i] = S.xb[gi][wm * 64 + 32 * i + l32];
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float p = (float)pi[mt][nt][r];
-                            if (FMT == 0)
-                                acc[mt][nt][r] += (xsv[r] * wsv[nt]) * p;
-                            else
-                                acc[mt][nt][r] += xsv[r] * (wsv[nt] * p) + xbv[r] * wbv[nt];
-                        }
+                for (int j = 0; j < 2; ++j) vb[j] = S.wb[gi][wn * 64 + 32 * j + l32];
+                if (bias_pending) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) va[i] = half ? va[i] : bva[i];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) vb[j] = half ? vb[j] : bvb[j];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int j = 0; j < 2; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[i], vb[j], acc[i][j], 0, 0, 0);
+                    bias_pending = false;
+                } else {
+                    bva[0] = va[0]; bva[1] = va[1];
+                    bvb[0] = vb[0]; bvb[1] = vb[1];
+                    bias_pending = true;
                 }
             }
         }
-    }
+    };
 
+    load_stage(0);
+    store_stage(stage_buf[0]);
+    if (nstages > 1) load_stage(1);
+    for (int st = 0; st < nstages; st += 2) {
+        do_stage(st, std::integral_constant<int, 0>());
+        if (st + 1 < nstages) do_stage(st + 1, std::integral_constant<int, 1>());
+    }
     if (!PARTIALS) {
+        if (BIAS_MFMA && bias_pending) {
+            float va[2], vb[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+            for (int i = 0; i < 2; ++i) va[i] = half ? 0.0f : bva[i];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int n = n0 + wn * 64 + nt * 32 + l32;
+            for (int j = 0; j < 2; ++j) vb[j] = half ? 0.0f : bvb[j];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[i], vb[j], acc[i][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int n = n0 + wn * 64 + 32 * j + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * 64 + mt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (m < M && n < N) y[(size_t)m * N + n] = acc[mt][nt][r];
+                    const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (m < M && n < N) y[(size_t)m * N + n] = acc[i][j][r];
                 }
             }
     }
@@ -242,15 +366,27 @@ template <int FMT, int G>
 hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                       hipStream_t stream) {
-    const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM)), block(256);
+    const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+    const size_t lds = 2 * sizeof(Stage<G, FMT>);
     const uint16_t* ws = static_cast<const uint16_t*>(wscale);
     const uint16_t* wb = static_cast<const uint16_t*>(wbias);
-    if (partials)
-        hipLaunchKernelGGL((gemm_kernel<FMT, G, true>), grid, block, 0, stream, M, K, N, wq, ws, wb, xq, xs, xsum,
-                           y, partials);
-    else
-        hipLaunchKernelGGL((gemm_kernel<FMT, G, false>), grid, block, 0, stream, M, K, N, wq, ws, wb, xq, xs, xsum,
-                           y, partials);
+    if (partials) {
+        auto k = gemm_kernel<FMT, G, true>;
+        static bool attr = false;
+        if (!attr) {
+            hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            attr = true;
+        }
+        hipLaunchKernelGGL(k, dim3(tiles), dim3(NT), lds, stream, M, K, N, wq, ws, wb, xq, xs, xsum, y, partials);
+    } else {
+        auto k = gemm_kernel<FMT, G, false>;
+        static bool attr = false;
+        if (!attr) {
+            hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            attr = true;
+        }
+        hipLaunchKernelGGL(k, dim3(tiles), dim3(NT), lds, stream, M, K, N, wq, ws, wb, xq, xs, xsum, y, partials);
+    }
     return hipGetLastError();
 }
 
