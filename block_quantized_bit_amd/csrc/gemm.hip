@@ -8,14 +8,12 @@
 // Tiling: a workgroup of 2 x 2 wavefronts computes a 128 x 128 tile of Y; each
 // wavefront owns 2 x 2 tiles of v_mfma_i32_32x32x32_i8 (32 x 32 outputs; one
 // 32-wide K step is one Q4_0 block). Two workgroups share a CU (registers are
-// held under 256 per lane and LDS under 80 KB per workgroup); they are not
-// synchronised with each other, so one's matrix work overlaps the other's
-// float rescale on every SIMD.
+// held under 256 per lane and LDS under 80 KB per workgroup).
 //
-// K is walked in 128-wide stages through two LDS buffers. The stage's global
-// loads are buffer loads with a per-lane offset fixed for the whole kernel
-// and the stage offset in a scalar register; rows past M or N read as zero
-// (the buffer range check), so the staging needs no masks. After the one
+// K is walked in 128-wide stages through two LDS tile buffers. The stage's
+// global loads are buffer loads with a per-lane offset fixed for the whole
+// kernel and the stage offset in a scalar register; rows past M or N read as
+// zero (the buffer range check), so the staging needs no masks. After the one
 // barrier of a stage, the registers holding stage s+1 are written to the free
 // buffer (weight nibbles unpacked on the way: q - 8 as signed bytes for Q4_0,
 // q for affine), the loads of stage s+2 are issued, and stage s is computed.
@@ -31,6 +29,15 @@
 // v_mfma_f32_32x32x2_f32 with two groups in its two K slots instead of a
 // fourth VALU op per output.
 //
+// The rescale is VALU work of the same order as the matrix work, so the two
+// are software-pipelined inside each wavefront: while the matrix core runs
+// the MFMA chain of one of the wavefront's four tiles for group g, the VALU
+// rescales the tile before it, whose integers are complete. Two int32 tiles
+// are live at a time instead of four, which pays for the registers the
+// overlap needs. Because the last tile's rescale trails its group into the
+// next stage, the per-stage scales sit in a ring of three LDS slots rather
+// than in the double-buffered tile memory.
+//
 // Workgroups are mapped to tiles so that the workgroups resident on one XCD
 // (dispatch is round-robin over the 8 XCDs) take neighbouring tiles, grouped
 // GROUP_M row tiles at a time, which keeps their shared A and B panels in
@@ -44,21 +51,29 @@ namespace q4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128;    // workgroup tile
 constexpr int KS = 128;              // K per stage
-constexpr int NT = 256;              // threads per workgroup
+constexpr int BM = 128, BN = 128;    // workgroup tile
+constexpr int NT = 256;              // threads per workgroup (2 x 2 wavefronts)
 constexpr int GROUP_M = 8;           // row tiles per tile group
 constexpr int NXCD = 8;
+constexpr int RING = 3;              // scale slots
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data format
 
+struct Tiles {
+    uint4 a[BM * KS / 16];  // int8 activation codes, swizzled 128-byte rows
+    uint4 b[BN * KS / 16];  // unpacked weight codes, swizzled 128-byte rows
+};
+
+// Scales of one stage. The staging threads cover SR = max(GPS, NT / 128) rows
+// of each array; rows past GPS only receive the zeros of threads with no
+// scale to stage, so the staging stores need no branch.
 template <int G, int FMT>
-struct Stage {
+struct Scales {
     static constexpr int GPS = KS / G;
-    static constexpr int NB = (FMT == 1) ? GPS : 1;  // affine keeps the bias operands too
-    uint4 a[BM * KS / 16];
-    uint4 b[BN * KS / 16];
-    float xs[GPS][BM];
-    float ws[GPS][BN];
+    static constexpr int SR = (GPS > NT / BM) ? GPS : NT / BM;
+    static constexpr int NB = (FMT == 1) ? SR : 1;  // affine keeps the bias operands too
+    float xs[SR][BM];
+    float ws[SR][BN];
     float xb[NB][BM];
     float wb[NB][BN];
 };
@@ -102,11 +117,10 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     constexpr int B_CH = BN * (KS / 32) / NT;  // 16-byte packed weight chunks per thread per stage (2)
     constexpr bool AFF = FMT == 1;
     constexpr bool BIAS_MFMA = AFF && !PARTIALS;
-    static_assert(A_CH * NT == BM * (KS / 16) && B_CH * NT == BN * (KS / 32), "tile / thread mismatch");
-
-    using St = Stage<G, FMT>;
+    using Sc = Scales<G, FMT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    St* stage_buf = reinterpret_cast<St*>(smem);
+    Tiles* tiles = reinterpret_cast<Tiles*>(smem);
+    Sc* ring = reinterpret_cast<Sc*>(smem + 2 * sizeof(Tiles));
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -139,8 +153,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
         const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
         off_b[i] = (n0 + c < N) ? (uint32_t)((n0 + c) * (K / 2) + b * 16) : OUT;
     }
-    // scale staging: the thread covers (gi, r) = divmod(tid + NT*i, BM), GPS*BM values
+    // scale staging: the thread covers (gi, r) = divmod(tid + NT*i, 128) of the
+    // GPS*128 activation scales and of the GPS*128 weight scales
+    static_assert(BM == BN, "scale staging assumes a square tile");
     constexpr int SC_N = (GPS * BM + NT - 1) / NT;
+    static_assert(SC_N * NT <= Sc::SR * BM, "scale staging overruns its rows");
     uint32_t off_xs[SC_N], off_ws[SC_N];
 #pragma unroll
     for (int i = 0; i < SC_N; ++i) {
@@ -189,11 +206,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
         }
     };
 
-    auto store_stage = [&](St& S) {
+    auto store_stage = [&](Tiles& T, Sc& S) {
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
             const int idx = tid + NT * i, r = idx >> 3, c16 = idx & 7;
-            S.a[swz(r, c16)] = ra[i];
+            T.a[swz(r, c16)] = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
@@ -204,27 +221,28 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
                 lo = make_uint4(minus8_bytes(lo.x), minus8_bytes(lo.y), minus8_bytes(lo.z), minus8_bytes(lo.w));
                 hi = make_uint4(minus8_bytes(hi.x), minus8_bytes(hi.y), minus8_bytes(hi.z), minus8_bytes(hi.w));
             }
-            S.b[swz(c, 2 * b)] = lo;      // k = 32b .. 32b+15
-            S.b[swz(c, 2 * b + 1)] = hi;  // k = 32b+16 .. 32b+31
+            T.b[swz(c, 2 * b)] = lo;      // k = 32b .. 32b+15
+            T.b[swz(c, 2 * b + 1)] = hi;  // k = 32b+16 .. 32b+31
         }
         if (!PARTIALS) {
 #pragma unroll
             for (int i = 0; i < SC_N; ++i) {
-                const int idx = tid + NT * i;
-                if (idx < GPS * BM) {
-                    const int gi = idx / BM, r = idx % BM;
-                    S.xs[gi][r] = rxs[i];
-                    S.ws[gi][r] = AFF ? bf16_to_float(rws[i]) : half_to_float(rws[i]);
-                    if (AFF) {
-                        S.xb[gi][r] = rxs[i] * (float)rxsum[i];
-                        S.wb[gi][r] = bf16_to_float(rwb[i]);
-                    }
+                const int idx = tid + NT * i, gi = idx / BM, r = idx % BM;
+                S.xs[gi][r] = rxs[i];
+                S.ws[gi][r] = AFF ? bf16_to_float(rws[i]) : half_to_float(rws[i]);
+                if (AFF) {
+                    S.xb[gi][r] = rxs[i] * (float)rxsum[i];
+                    S.wb[gi][r] = bf16_to_float(rwb[i]);
                 }
             }
         }
     };
 
     // ---------------------------------------------------------------- compute
+    // The wavefront's four 32 x 32 tiles (i, j) -- rows wm*64 + 32i, columns
+    // wn*64 + 32j -- are visited in the order (0,0) (0,1) (1,1) (1,0), so that
+    // consecutive tiles share a fragment. Phase t of a group runs tile t's MFMA
+    // chain into pi[t & 1] while the VALU rescales tile t - 1 from pi[(t+1) & 1].
     v16f acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -232,130 +250,174 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
         for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    v16i pi[2];
 
-    const int arow0 = wm * 64 + l32, brow0 = wn * 64 + l32;
-    float bva[2] = {0.0f, 0.0f}, bvb[2] = {0.0f, 0.0f};  // bias operands of a pending slot-0 group
-    bool bias_pending = false;
+    const int arow = wm * 64 + l32;       // fragment row of A (+ 32i); also the bias row of xb
+    const int brow = wn * 64 + l32;       // fragment row of B (+ 32j): this lane's output column
+    const int xrow = wm * 64 + 4 * half;  // first output row of this lane (+ 32i + 8q + r)
 
-    auto do_stage = [&](int st, auto par) {
-        constexpr int P = decltype(par)::value;
-        __syncthreads();
-        if (st + 1 < nstages) store_stage(stage_buf[P ^ 1]);
-        if (st + 2 < nstages) load_stage(st + 2);
-        const St& S = stage_buf[P];
-        const int k0 = st * KS;
-        const int ks = min(KS, K - k0);
+    auto frag = [&](const uint4* base, int row, int gi, int s) {
+        return __builtin_bit_cast(v4i, base[swz(row, gi * (G / 16) + 2 * s + half)]);
+    };
+
+    // MFMA chain of one group for one tile.
+    auto mfma_tile = [&](v16i& d, const v4i (&fa)[SPG], const v4i (&fb)[SPG]) {
+        const v16i z = {};
+        d = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fb[0], z, 0, 0, 0);
 #pragma unroll
-        for (int gi = 0; gi < GPS; ++gi) {
-            if (gi * G >= ks) break;
-            v16i pi[2][2];
+        for (int s = 1; s < SPG; ++s) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s], fb[s], d, 0, 0, 0);
+    };
+
+    // Activation scales of this lane's 16 rows in strip i (slot gi of S); the
+    // two tiles of a strip share them.
+    auto read_xs = [&](float (&xsv)[16], const Sc& S, int gi, int i) {
+        if (PARTIALS) return;
 #pragma unroll
-            for (int s = 0; s < SPG; ++s) {
-                const int chunk = gi * (G / 16) + 2 * s + half;
-                v4i af[2], bf[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) af[i] = __builtin_bit_cast(v4i, S.a[swz(arow0 + 32 * i, chunk)]);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) bf[j] = __builtin_bit_cast(v4i, S.b[swz(brow0 + 32 * j, chunk)]);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        if (s == 0) {
-                            const v16i z = {};
-                            pi[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], z, 0, 0, 0);
-                        } else {
-                            pi[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], pi[i][j], 0, 0, 0);
-                        }
-                    }
-            }
-            // D layout of the 32x32 MFMA: lane holds column l32, rows 8*(r/4) + 4*half + r%4.
-            if (PARTIALS) {
-                const int g = k0 / G + gi;
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int n = n0 + wn * 64 + 32 * j + l32;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-                            if (m < M && n < N) partials[((size_t)m * N + n) * ngroups + g] = pi[i][j][r];
-                        }
-                    }
-                continue;
-            }
-            float wsv[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) wsv[j] = S.ws[gi][wn * 64 + 32 * j + l32];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                float xsv[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(&S.xs[gi][wm * 64 + 32 * i + 8 * q + 4 * half]);
-                    xsv[4 * q] = v.x; xsv[4 * q + 1] = v.y; xsv[4 * q + 2] = v.z; xsv[4 * q + 3] = v.w;
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[i][j][r] += xsv[r] * (wsv[j] * (float)pi[i][j][r]);
-            }
-            if (BIAS_MFMA) {
-                // two groups per f32 MFMA: lanes of half h supply group slot h
-                float va[2], vb[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) va[i] = S.xb[gi][wm * 64 + 32 * i + l32];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) vb[j] = S.wb[gi][wn * 64 + 32 * j + l32];
-                if (bias_pending) {
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) va[i] = half ? va[i] : bva[i];
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) vb[j] = half ? vb[j] : bvb[j];
-#pragma unroll
-                    for (int i = 0; i < 2; ++i)
-#pragma unroll
-                        for (int j = 0; j < 2; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[i], vb[j], acc[i][j], 0, 0, 0);
-                    bias_pending = false;
-                } else {
-                    bva[0] = va[0]; bva[1] = va[1];
-                    bvb[0] = vb[0]; bvb[1] = vb[1];
-                    bias_pending = true;
-                }
-            }
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4*>(&S.xs[gi][xrow + 32 * i + 8 * q]);
+            xsv[4 * q] = v.x; xsv[4 * q + 1] = v.y; xsv[4 * q + 2] = v.z; xsv[4 * q + 3] = v.w;
         }
     };
 
-    load_stage(0);
-    store_stage(stage_buf[0]);
-    if (nstages > 1) load_stage(1);
-    for (int st = 0; st < nstages; st += 2) {
-        do_stage(st, std::integral_constant<int, 0>());
-        if (st + 1 < nstages) do_stage(st + 1, std::integral_constant<int, 1>());
-    }
+    // Rescale tile (i, j)'s integers of group g (slot gi of scale set S, xsv
+    // from read_xs) into acc, or store them as partials. D layout of the 32x32
+    // MFMA: lane holds column l32, rows 8*(r/4) + 4*half + r%4.
+    auto rescale_tile = [&](const v16i& d, const float (&xsv)[16], const Sc& S, int gi, int i, int j, int g) {
+        if (PARTIALS) {
+            // row r of the lane's 16 sits (8*(r/4) + r%4) rows below its first row;
+            // the row stride is wave-uniform, so the offsets stay in scalar registers
+            const int n = n0 + brow + 32 * j;
+            const int mb = m0 + xrow + 32 * i;
+            const size_t rstride = (size_t)__builtin_amdgcn_readfirstlane(N * ngroups);
+            int32_t* pb = partials + ((size_t)mb * N + n) * ngroups + g;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dr = 8 * (r >> 2) + (r & 3);
+                if (mb + dr < M && n < N && g < ngroups) pb[dr * rstride] = d[r];
+            }
+            return;
+        }
+        const float w = S.ws[gi][brow + 32 * j];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += xsv[r] * (w * (float)d[r]);
+    };
+
+    // Affine bias of two groups on the f32 matrix core for tile (i, j): lanes
+    // of half 0 supply group slot 0 (S0, gi0), lanes of half 1 group slot 1
+    // (S1, gi1), or zero when that slot is empty.
+    auto bias_tile = [&](const Sc& S0, int gi0, const Sc& S1, int gi1, int i, int j, bool second) {
+        const Sc& S = half ? S1 : S0;
+        const int gi = half ? gi1 : gi0;
+        const bool on = !half || second;
+        const float va = on ? S.xb[gi][arow + 32 * i] : 0.0f;
+        const float vb = on ? S.wb[gi][brow + 32 * j] : 0.0f;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, vb, acc[i][j], 0, 0, 0);
+    };
+
+    int g = 0;  // global index of the next group
+    int rs = 0, rs_prev = RING - 1;  // ring slots of the current and the previous stage
+    // The first phase rescales tile (1,0) of a group "-1": its integers are zero
+    // and the scale slot standing for stage -1 is zeroed, so it adds exactly zero
+    // and the pipeline needs no branch.
+    pi[1] = v16i{};
+    float xs0[16], xs1[16];  // activation scales of strip 0 (current group) and strip 1 (held into the next group)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xs1[r] = 0.0f;
     if (!PARTIALS) {
-        if (BIAS_MFMA && bias_pending) {
-            float va[2], vb[2];
+        float* z = reinterpret_cast<float*>(&ring[RING - 1]);
+        for (int i = tid; i < (int)(sizeof(Sc) / 4); i += NT) z[i] = 0.0f;
+    }
+
+    // One stage. The stage is straight-line code: stages and groups past the
+    // end of K are staged and computed like the others, from loads that read
+    // zero (codes and scales alike), so they add exactly zero.
+    auto do_stage = [&](int st, auto par) {
+        constexpr int P = decltype(par)::value;
+        __syncthreads();
+        const int rs_next = (rs + 1 == RING) ? 0 : rs + 1;
+        store_stage(tiles[P ^ 1], ring[rs_next]);
+        load_stage(st + 2);
+        const Tiles& T = tiles[P];
+        const Sc& S = ring[rs];
+        const Sc& Sp = ring[rs_prev];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) va[i] = half ? 0.0f : bva[i];
+        for (int gi = 0; gi < GPS; ++gi) {
+            // group g - 1: earlier in this stage, or the last group of the previous stage
+            const Sc& S1 = gi == 0 ? Sp : S;
+            const int gi1 = gi == 0 ? GPS - 1 : gi - 1;
+            // bias groups pair up as (g - 1, g) for odd g = st*GPS + gi; stages alternate P
+            const bool odd = (GPS == 1) ? (P == 1) : ((gi & 1) == 1);
+            v4i fa0[SPG], fa1[SPG], fb0[SPG], fb1[SPG];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) vb[j] = half ? 0.0f : bvb[j];
+            for (int s2 = 0; s2 < SPG; ++s2) {
+                fa0[s2] = frag(T.a, arow, gi, s2);
+                fb0[s2] = frag(T.b, brow, gi, s2);
+            }
+            // phase 0: tile (0,0) of group g; rescale tile (1,0) of group g - 1
+            mfma_tile(pi[0], fa0, fb0);
+            if (BIAS_MFMA && odd) bias_tile(S1, gi1, S, gi, 0, 0, true);
+            if (!PARTIALS || g > 0) rescale_tile(pi[1], xs1, S1, gi1, 1, 0, g - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // phase 1: tile (0,1); rescale tile (0,0)
+#pragma unroll
+            for (int s2 = 0; s2 < SPG; ++s2) fb1[s2] = frag(T.b, brow + 32, gi, s2);
+            mfma_tile(pi[1], fa0, fb1);
+            if (BIAS_MFMA && odd) bias_tile(S1, gi1, S, gi, 0, 1, true);
+            read_xs(xs0, S, gi, 0);
+            rescale_tile(pi[0], xs0, S, gi, 0, 0, g);
+            __builtin_amdgcn_sched_barrier(0);
+            // phase 2: tile (1,1); rescale tile (0,1)
+#pragma unroll
+            for (int s2 = 0; s2 < SPG; ++s2) fa1[s2] = frag(T.a, arow + 32, gi, s2);
+            mfma_tile(pi[0], fa1, fb1);
+            if (BIAS_MFMA && odd) bias_tile(S1, gi1, S, gi, 1, 1, true);
+            rescale_tile(pi[1], xs0, S, gi, 0, 1, g);
+            __builtin_amdgcn_sched_barrier(0);
+            // phase 3: tile (1,0); rescale tile (1,1)
+            mfma_tile(pi[1], fa1, fb0);
+            if (BIAS_MFMA && odd) bias_tile(S1, gi1, S, gi, 1, 0, true);
+            read_xs(xs1, S, gi, 1);
+            rescale_tile(pi[0], xs1, S, gi, 1, 1, g);
+            __builtin_amdgcn_sched_barrier(0);
+            ++g;
+        }
+        rs_prev = rs;
+        rs = rs_next;
+    };
+
+    load_stage(0);
+    store_stage(tiles[0], ring[0]);
+    load_stage(1);
+    int st = 0;
+    for (; st + 1 < nstages; st += 2) {
+        do_stage(st, std::integral_constant<int, 0>());
+        do_stage(st + 1, std::integral_constant<int, 1>());
+    }
+    if (st < nstages) do_stage(st, std::integral_constant<int, 0>());
+    // tile (1,0) of the last group of the last stage (whose scales are in that
+    // stage's slot); with one group per stage and an odd stage count the last
+    // group's bias has no partner group
+    {
+        const Sc& Sl = ring[rs_prev];
+        const int gl = nstages * GPS - 1;
+        rescale_tile(pi[1], xs1, Sl, GPS - 1, 1, 0, gl);
+        if (BIAS_MFMA && GPS == 1 && (nstages & 1)) {
+            const int gil = GPS - 1;
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(va[i], vb[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 2; ++j) bias_tile(Sl, gil, Sl, gil, i, j, false);
         }
+    }
+    if (!PARTIALS) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int n = n0 + wn * 64 + 32 * j + l32;
+                const int n = n0 + brow + 32 * j;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+                    const int m = m0 + xrow + 32 * i + 8 * (r >> 2) + (r & 3);
                     if (m < M && n < N) y[(size_t)m * N + n] = acc[i][j][r];
                 }
             }
@@ -366,27 +428,18 @@ template <int FMT, int G>
 hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                       hipStream_t stream) {
-    const unsigned tiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-    const size_t lds = 2 * sizeof(Stage<G, FMT>);
+    const unsigned ntiles = (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+    const size_t lds = 2 * sizeof(Tiles) + RING * sizeof(Scales<G, FMT>);
     const uint16_t* ws = static_cast<const uint16_t*>(wscale);
     const uint16_t* wb = static_cast<const uint16_t*>(wbias);
-    if (partials) {
-        auto k = gemm_kernel<FMT, G, true>;
-        static bool attr = false;
-        if (!attr) {
-            hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            attr = true;
-        }
-        hipLaunchKernelGGL(k, dim3(tiles), dim3(NT), lds, stream, M, K, N, wq, ws, wb, xq, xs, xsum, y, partials);
-    } else {
-        auto k = gemm_kernel<FMT, G, false>;
-        static bool attr = false;
-        if (!attr) {
-            hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            attr = true;
-        }
-        hipLaunchKernelGGL(k, dim3(tiles), dim3(NT), lds, stream, M, K, N, wq, ws, wb, xq, xs, xsum, y, partials);
+    auto k = partials ? gemm_kernel<FMT, G, true> : gemm_kernel<FMT, G, false>;
+    static bool attr[2] = {false, false};
+    if (!attr[partials != nullptr]) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+        attr[partials != nullptr] = true;
     }
+    hipLaunchKernelGGL(k, dim3(ntiles), dim3(NT), lds, stream, M, K, N, wq, ws, wb, xq, xs, xsum, y, partials);
     return hipGetLastError();
 }
 
