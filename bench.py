@@ -46,8 +46,8 @@ def parse_args():
     p.add_argument("--no-secondary", action="store_true", help="headline decode line only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
-                   help="run one secondary workload alone (for profiling): gemm_3a, gemm_3b, gemm_2, gemm_0, "
-                        "q4k_gemv, q4k_gemm, act_quant, gemv_plain")
+                   help="run one workload alone (for profiling): gemv_fused (eager decode launches, --steps of "
+                        "them), gemm_3a, gemm_3b, gemm_2, gemm_0, q4k_gemv, q4k_gemm, act_quant, gemv_plain")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run a plain device-to-device copy of this many MiB (counter calibration) and exit")
     return p.parse_args()
@@ -139,6 +139,13 @@ def main():
         q4.gemv_fused("q4_0", 32, x, c[0], c[1], None, y=y)
 
     result = {}
+    if args.only == "gemv_fused":
+        # eager launches over the cold copies, for counter collection (one dispatch per step)
+        for i in range(args.steps):
+            decode_step(i)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "gemv_fused", "launches": args.steps}), flush=True)
+        return
     if args.only is None:
         for i in range(min(args.warmup, GRAPH_STEPS)):
             decode_step(i)
