@@ -47,7 +47,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default=None,
                    help="run one workload alone (for profiling): gemv_fused (eager decode launches, --steps of "
-                        "them), gemm_3a, gemm_3b, gemm_2, gemm_0, q4k_gemv, q4k_gemm, act_quant, gemv_plain")
+                        "them), gemm_3a, gemm_3b, gemm_2, gemm_0, q4k_gemv, q4k_gemm, act_quant, gemv_plain, "
+                        "small_m")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run a plain device-to-device copy of this many MiB (counter calibration) and exit")
     return p.parse_args()
@@ -238,6 +239,35 @@ def main():
         secondary["gemv_plain_q4_0_decode_4096"] = {
             "what": "q4_gemv (activation codes given), cold weights, HIP graph", "us": round(t * 1e6, 3),
             "GB/s": round(weight_bytes / t / 1e9, 1), "frac_hbm": round(weight_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if want("small_m"):
+        # few-row decode: M rows of decode-like activations against the same cold weight copies
+        rows = {}
+        for M in (2, 4, 8, 16, 32):
+            xm = torch.from_numpy(synth.gen.activations(wl, M=M)).to(dev)
+            xq_m, xs_m, xsum_m = q4.quantize_act(xm, 32)
+            y_m = torch.empty((M, wl.N), dtype=torch.float32, device=dev)
+
+            def few(i, xq_m=xq_m, xs_m=xs_m, xsum_m=xsum_m, y_m=y_m):
+                c = copies[i % GRAPH_STEPS]
+                q4.gemm("q4_0", 32, c[0], c[1], None, xq_m, xs_m, xsum_m, y=y_m)
+            few(0)
+            g = graph_of(few, GRAPH_STEPS)
+            g.replay()
+            e0, e1 = event_pair()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / (10 * GRAPH_STEPS)
+            rows[str(M)] = {"us": round(t * 1e6, 3), "GB/s": round(weight_bytes / t / 1e9, 1),
+                            "frac_hbm": round(weight_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                            "TOPS": round(2.0 * M * wl.K * wl.N / t / 1e12, 2)}
+        secondary["small_m_q4_0_rows_x4096x4096"] = {
+            "what": "q4_gemm with M rows (few-row kernel: each weight block read once for all rows), cold weights, "
+                    "HIP graph; activation codes given", "by_M": rows}
 
     del copies
 

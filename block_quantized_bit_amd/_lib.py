@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libq4.so")
 
 Q4_DT_F32, Q4_DT_BF16 = 0, 1
 Q4_FMT_Q4_0, Q4_FMT_AFFINE = 0, 1
-Q4_PATH_GEMV, Q4_PATH_GEMM = 0, 1
+Q4_PATH_GEMV, Q4_PATH_GEMM, Q4_PATH_SMALL = 0, 1, 2
 Q4K_BLOCK_BYTES = 144
 
 EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
@@ -160,14 +160,15 @@ def gemm(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int =
 
 def debug_partials(path: str, fmt: str, bs: int, wq, xq, xsum, m0: int = 0, m1: int | None = None, out=None,
                    bits: int = 4, stream=None):
-    """Exact per-block int32 partials [(m1-m0)][N][K/bs] from the GEMV ('gemv') or GEMM ('gemm') kernel."""
+    """Exact per-block int32 partials [(m1-m0)][N][K/bs] from the GEMV ('gemv'), tiled GEMM ('gemm') or
+    few-row GEMM ('small') kernel."""
     N, Kh = wq.shape
     K = 2 * Kh
     M = xq.shape[0]
     m1 = M if m1 is None else m1
     if out is None:
         out = torch.empty((max(m1 - m0, 1), N, K // bs), dtype=torch.int32, device=wq.device)
-    p = {"gemv": Q4_PATH_GEMV, "gemm": Q4_PATH_GEMM}[path]
+    p = {"gemv": Q4_PATH_GEMV, "gemm": Q4_PATH_GEMM, "small": Q4_PATH_SMALL}[path]
     _check(lib().q4_debug_partials(p, M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(xq), _ptr(xsum), m0, m1,
                                    _ptr(out), _stream(stream)), "q4_debug_partials")
     return out

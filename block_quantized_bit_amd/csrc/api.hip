@@ -109,6 +109,10 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, c
     if ((long long)M * K >= (1LL << 31) || (long long)N * (K / 2) >= (1LL << 31)) return Q4_ERR_DIM;
     st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
     if (st) return st;
+    // a few rows: stream every weight block once for all of them
+    if (M <= q4::GEMM_SMALL_MAX_M && K <= q4::GEMM_SMALL_MAX_K)
+        return hip_status(q4::launch_gemm_small(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
+                                                static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemm(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
                                       static_cast<hipStream_t>(stream)));
 }
@@ -117,7 +121,7 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
                       const int32_t* xsum, int m0, int m1, int32_t* partials, void* stream) {
     int st = matmul_status(M, K, N, bs, fmt, bits);
     if (st) return st;
-    if (path != Q4_PATH_GEMV && path != Q4_PATH_GEMM) return Q4_ERR_FORMAT;
+    if (path != Q4_PATH_GEMV && path != Q4_PATH_GEMM && path != Q4_PATH_SMALL) return Q4_ERR_FORMAT;
     if (!wq || !xq || !xsum || !partials) return Q4_ERR_NULL;
     if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(xsum, 4) || !aligned(partials, 4)) return Q4_ERR_ALIGN;
     if (m0 < 0 || m1 > M || m0 >= m1) return Q4_ERR_RANGE;
@@ -131,6 +135,12 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
         if (K > Q4_GEMV_MAX_K) return Q4_ERR_DIM;
         return hip_status(q4::launch_gemv(K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
                                           partials, s));
+    }
+    if (path == Q4_PATH_SMALL) {
+        if (m1 - m0 > q4::GEMM_SMALL_MAX_M) return Q4_ERR_RANGE;
+        if (K > q4::GEMM_SMALL_MAX_K) return Q4_ERR_DIM;
+        return hip_status(q4::launch_gemm_small(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0,
+                                                nullptr, partials, s));
     }
     return hip_status(q4::launch_gemm(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
                                       partials, s));

@@ -75,7 +75,7 @@ enum {
     Q4_FMT_Q4_0 = 0,     /* bs = 32; wscale fp16 [N][K/32]; wbias unused (may be NULL) */
     Q4_FMT_AFFINE = 1    /* bs = g in {64, 128}; wscale, wbias bf16 [N][K/g] */
 };
-enum { Q4_PATH_GEMV = 0, Q4_PATH_GEMM = 1 };
+enum { Q4_PATH_GEMV = 0, Q4_PATH_GEMM = 1, Q4_PATH_SMALL = 2 };
 
 /*
  * Per-block int8 quantization of activations (tract PR #2432: "activation ->
@@ -125,9 +125,16 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
 
 /*
  * Prefill GEMM, any M >= 1: Y[m][n] as q4_gemv for every row m, computed on
- * the int8 matrix cores (32x32x32 int8 MFMA, one 32-weight block per K-step,
- * int32 accumulation within a block or group, float rescale per block).
- * Same arguments as q4_gemv with xq [M][K], xs, xsum [M][K/bs], y [M][N].
+ * the int8 matrix cores (int32 accumulation within a block or group, float
+ * rescale per block). Same arguments as q4_gemv with xq [M][K], xs, xsum
+ * [M][K/bs], y [M][N]. M*K and N*K/2 must be below 2^31.
+ * Two kernels, chosen by M:
+ *   M <= 32 and K <= 32768: every weight block is read once for all rows
+ *     (16x16x32 int8 MFMA, 16 output columns per workgroup, K split over its
+ *     wavefronts). tract PR #2432 measures decode-sized products as weight
+ *     streams; MLX PR #4802 leaves its int8 path below M = 32.
+ *   otherwise: 128 x 128 output tiles on 32x32x32 int8 MFMA, one 32-weight
+ *     block per K step.
  */
 int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
             const uint8_t* wq, const void* wscale, const void* wbias,
@@ -136,8 +143,10 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
 
 /*
  * Debug view of the exact integer partials computed inside q4_gemv
- * (path Q4_PATH_GEMV, needs M == 1) or q4_gemm (Q4_PATH_GEMM): the same
- * kernels, compiled with the partials store in place of the float epilogue.
+ * (path Q4_PATH_GEMV, needs M == 1) or q4_gemm (Q4_PATH_GEMM: the tiled
+ * kernel, any row count; Q4_PATH_SMALL: the few-row kernel, m1 - m0 <= 32 and
+ * K <= 32768, else Q4_ERR_RANGE / Q4_ERR_DIM): the same kernels, compiled
+ * with the partials store in place of the float epilogue.
  * partials [(m1-m0)][N][K/bs] int32 for rows m0 <= m < m1:
  *   Q4_0:   sum_{k in b} (q - 8) * xq[m][k]
  *   affine: sum_{k in g} q * xq[m][k]

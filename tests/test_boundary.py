@@ -103,7 +103,8 @@ def test_debug_partials_validation():
     f = q4.lib().q4_debug_partials
     base = [1, 4, 128, 8, 32, 0, 4, A, A, A, 0, 4, A, None]
     assert f(*base[:6], 8, *base[7:]) == FORMAT          # bits
-    assert f(2, *base[1:]) == FORMAT                     # path
+    assert f(3, *base[1:]) == FORMAT                     # path
+    assert f(-1, *base[1:]) == FORMAT
     args = list(base); args[10], args[11] = 2, 2
     assert f(*args) == RANGE                             # empty range
     args = list(base); args[11] = 5
@@ -112,6 +113,11 @@ def test_debug_partials_validation():
     assert f(*args) == RANGE                             # GEMV path needs one row
     args = list(base); args[12] = None
     assert f(*args) == NULL
+    # few-row kernel: at most 32 rows and K <= 32768
+    big = [2, 40, 128, 8, 32, 0, 4, A, A, A, 0, 33, A, None]
+    assert f(*big) == RANGE
+    big[11] = 32; big[2] = 65536
+    assert f(*big) == DIM
 
 
 def test_q4k_validation():

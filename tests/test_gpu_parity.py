@@ -288,6 +288,95 @@ def test_gemm_deterministic():
     assert torch.equal(y1, y2)
 
 
+# ---------------------------------------------------------------- few-row GEMM (M <= 32)
+
+SMALL_CASES = [("q4_0", 32, 2, 416, 37), ("q4_0", 32, 16, 96, 17), ("q4_0", 32, 17, 4096, 33),
+               ("q4_0", 32, 32, 8224, 16), ("affine", 64, 5, 320, 31), ("affine", 64, 32, 4096, 48),
+               ("affine", 128, 3, 14336, 21), ("affine", 128, 24, 384, 129)]
+
+
+@pytest.mark.parametrize("fmt,bs,M,K,N", SMALL_CASES)
+def test_small_partials_bit_exact(fmt, bs, M, K, N):
+    print(f"case small partials {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, M, K, N, 7 * M + K + N)
+    ref = oracle.q4_partials(wts[0], act[0], K, N, bs, FMT[fmt])
+    got = q4.debug_partials("small", fmt, bs, to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]))
+    _sync()
+    assert np.array_equal(to_np(got), ref)
+
+
+@pytest.mark.parametrize("fmt,bs,M,K,N", SMALL_CASES)
+def test_small_gemm_ragged(fmt, bs, M, K, N):
+    print(f"case small gemm {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, M, K, N, 7 * M + K + N)
+    y = q4.gemm(fmt, bs, *_wts_dev(fmt, wts), *[to_dev(a) for a in act])   # M <= 32: the few-row kernel
+    _sync()
+    assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+
+
+@pytest.mark.parametrize("M", [2, 4, 8, 16, 32])
+def test_small_gemm_decode_rows(M):
+    # the decode workload's weights against M rows drawn like its activation vector
+    print(f"case small gemm q4_0 decode rows M={M}", flush=True)
+    wl, _, _, _, wts = workload_data("q4_0_decode_4096")
+    x = synth.gen.activations(wl, M=M)
+    act = oracle.quantize_act(x, 32)
+    gq, gs, gsum = q4.quantize_act(to_dev(x), 32)
+    y = q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), gq, gs, gsum)
+    _sync()
+    assert np.array_equal(to_np(gq), act[0]) and np.array_equal(to_np(gs).view(np.uint32), act[1].view(np.uint32))
+    assert rel_rms(to_np(y), _oracle_y("q4_0", wts, act, wl.K, wl.N, 32)) <= TOL
+
+
+def test_small_gemm_dispatch_boundary():
+    # 32 rows take the few-row kernel, 33 the tiled one; both against the oracle
+    print("case small/tiled boundary M=32,33", flush=True)
+    wts, act = _partials_case("affine", 64, 33, 1024, 200, 4242)
+    g = _wts_dev("affine", wts)
+    ref = _oracle_y("affine", wts, act, 1024, 200, 64)
+    y33 = q4.gemm("affine", 64, *g, *[to_dev(a) for a in act])
+    y32 = q4.gemm("affine", 64, *g, *[to_dev(a[:32]) for a in act])
+    _sync()
+    assert rel_rms(to_np(y33), ref) <= TOL
+    assert rel_rms(to_np(y32), ref[:32]) <= TOL
+
+
+@pytest.mark.parametrize("fmt,bs,M,N", [("q4_0", 32, 32, 16), ("affine", 64, 17, 20)])
+def test_small_gemm_max_k(fmt, bs, M, N):
+    # K = 32768: the activation scales of all rows fill 144 KB of LDS (Q4_0, 32 rows)
+    print(f"case small gemm max K {fmt} M={M} N={N}", flush=True)
+    K = 32768
+    wts, act = _partials_case(fmt, bs, M, K, N, 99 + M)
+    y = q4.gemm(fmt, bs, *_wts_dev(fmt, wts), *[to_dev(a) for a in act])
+    p = q4.debug_partials("small", fmt, bs, to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]))
+    _sync()
+    assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+    assert np.array_equal(to_np(p), oracle.q4_partials(wts[0], act[0], K, N, bs, FMT[fmt]))
+
+
+@pytest.mark.parametrize("fmt,bs,K,N", [("q4_0", 32, 4096, 4096), ("affine", 128, 14336, 33)])
+def test_small_partials_equal_gemv_partials(fmt, bs, K, N):
+    print(f"case small/gemv partials {fmt} bs={bs} K={K} N={N}", flush=True)
+    wts, act = _partials_case(fmt, bs, 1, K, N, K + 3 * N)
+    args = (to_dev(wts[0]), to_dev(act[0]), to_dev(act[2]))
+    ps = q4.debug_partials("small", fmt, bs, *args)
+    pv = q4.debug_partials("gemv", fmt, bs, *args)
+    _sync()
+    assert torch.equal(ps, pv)
+    assert np.array_equal(to_np(ps), oracle.q4_partials(wts[0], act[0], K, N, bs, FMT[fmt]))
+
+
+def test_small_gemm_deterministic():
+    print("case small gemm determinism", flush=True)
+    wts, act = _partials_case("q4_0", 32, 24, 4096, 300, 5150)
+    g = _wts_dev("q4_0", wts)
+    a = [to_dev(v) for v in act]
+    y1 = q4.gemm("q4_0", 32, *g, *a)
+    y2 = q4.gemm("q4_0", 32, *g, *a)
+    _sync()
+    assert torch.equal(y1, y2)
+
+
 # ---------------------------------------------------------------- Q4_K
 
 def test_q4k_gemv_workload():
