@@ -110,7 +110,7 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, c
     st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
     if (st) return st;
     // a few rows: stream every weight block once for all of them
-    if (M <= q4::GEMM_SMALL_MAX_M && K <= q4::GEMM_SMALL_MAX_K)
+    if (M <= q4::GEMM_SMALL_MAX_M)
         return hip_status(q4::launch_gemm_small(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
                                                 static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemm(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
@@ -138,7 +138,6 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
     }
     if (path == Q4_PATH_SMALL) {
         if (m1 - m0 > q4::GEMM_SMALL_MAX_M) return Q4_ERR_RANGE;
-        if (K > q4::GEMM_SMALL_MAX_K) return Q4_ERR_DIM;
         return hip_status(q4::launch_gemm_small(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0,
                                                 nullptr, partials, s));
     }

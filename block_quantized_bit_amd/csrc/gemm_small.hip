@@ -7,11 +7,14 @@
 // instead; here the int8 path covers every M.
 //
 // A workgroup owns 16 output columns and all M rows, so every weight block is
-// read once for all rows. Its 8 wavefronts split K into contiguous ranges of
-// whole blocks or groups; each runs v_mfma_i32_16x16x32_i8 (16 rows x 16
-// columns x one 32-weight block) per K step, with one or two 16-row tiles.
-// The wavefronts' float partial sums are added in LDS in a fixed order (no
-// atomics, so results do not depend on scheduling).
+// read once for all rows. K is walked in chunks of 2048: the workgroup copies
+// the chunk's packed codes (16 rows x 1 KB), activation codes (M rows x 2 KB)
+// and activation scales into LDS with coalesced 128-bit loads (the next
+// chunk's loads are in flight while this one is computed), then its 8
+// wavefronts split the chunk's 64 K steps; each runs v_mfma_i32_16x16x32_i8
+// (16 rows x 16 columns x one 32-weight block) per step, with one or two
+// 16-row tiles. The wavefronts' float partial sums are added in LDS in a
+// fixed order (no atomics, so results do not depend on scheduling).
 //
 // Operands of the 16x16x32 int8 MFMA (lane l, q = l / 16): A holds row l % 16
 // and k = 8q .. 8q+7 of the step; B holds column l % 16 and the same k; D
@@ -23,7 +26,9 @@
 // Rescale after each block (Q4_0) or group (affine, 2 or 4 MFMA steps):
 //   acc += xs[m] * (d[n] * P)          Q4_0 (P from codes q - 8)
 //   acc += xs[m] * (s[n] * A) + (xs * xsum)[m] * b[n]   affine
-// The activation scales (and xs * xsum) of all rows are staged in LDS once.
+// The activation scales (and xs * xsum) of a chunk are staged with its codes.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -31,16 +36,31 @@ namespace q4 {
 
 namespace {
 
-constexpr int SW = 8;          // wavefronts per workgroup, each with a contiguous K range
+constexpr int SW = 8;          // wavefronts per workgroup
 constexpr int SNT = 64 * SW;   // threads per workgroup
 constexpr int SN = 16;         // output columns per workgroup
-constexpr int PS = 16;         // K steps whose loads are issued together
+// K per chunk staged in LDS: 2048 with one 16-row tile, 1024 with two (the
+// activation codes of a chunk and two chunks of loads in flight stay within
+// the register and LDS budget).
+template <int MT>
+constexpr int chunk_k() { return MT == 1 ? 2048 : 1024; }
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data format
 constexpr uint32_t OUT = 0x80000000u;   // beyond every buffer range: reads as zero
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
 }
+
+template <int G, int MT>
+struct SmallLds {
+    static constexpr int KC = chunk_k<MT>();
+    static constexpr int GPC = KC / G;  // groups per chunk
+    uint8_t w[SN][KC / 2 + 16];         // packed codes of the chunk (16 bytes of padding per row)
+    uint8_t a[16 * MT][KC + 16];        // activation codes of the chunk
+    float xs[GPC][16 * MT];             // activation scales, group-major
+    float xb[GPC][16 * MT];             // xs * xsum (affine)
+    float red[SW][MT][256];             // per-wavefront partial sums
+};
 
 template <int FMT, int G, int MT, bool PARTIALS>
 __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
@@ -53,32 +73,101 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
     constexpr int SPG = G / 32;     // MFMA steps per block or group
     constexpr bool AFF = FMT == 1;
     constexpr int MR = 16 * MT;     // rows covered by the MFMA tiles
-    static_assert(PS % SPG == 0, "a load pass holds whole groups");
+    using L = SmallLds<G, MT>;
+    constexpr int KC = L::KC;
+    constexpr int GPC = L::GPC;
+    constexpr int SPW = KC / 32 / SW;  // MFMA steps per wavefront per chunk
+    static_assert(SPW % SPG == 0, "a wavefront's share of a chunk holds whole groups");
+    constexpr int W_CH = SN * (KC / 2) / 16 / SNT;     // 16-byte weight loads per thread per chunk (2)
+    constexpr int A_CH = MR * KC / 16 / SNT;           // 16-byte activation loads per thread per chunk (4 / 8)
+    constexpr int S_CH = (MR * GPC + SNT - 1) / SNT;   // scale values per thread per chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    const int ngroups = K / G;
-    float* sxs = reinterpret_cast<float*>(smem);                  // [ngroups][MR]
-    float* sxb = sxs + (size_t)ngroups * MR;                      // [ngroups][MR], affine
-    float* red = sxs + (size_t)ngroups * MR * (AFF ? 2 : 1);      // [SW][MT][16 x 16]
+    L& S = *reinterpret_cast<L*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane >> 4, c = lane & 15;
-    const int n = blockIdx.x * SN + c;
-
-    // this wavefront's groups [gb, ge) and K steps [sb, se)
-    const int gpw = (ngroups + SW - 1) / SW;
-    const int gb = min(ngroups, wave * gpw), ge = min(ngroups, gb + gpw);
-    const int sb = gb * SPG, se = ge * SPG;
+    const int n0 = blockIdx.x * SN;
+    const int ngroups = K / G;
+    const int nchunks = (K + KC - 1) / KC;
 
     const __amdgpu_buffer_rsrc_t r_b = rsrc(wq, (uint32_t)((size_t)N * (K / 2)));
     const __amdgpu_buffer_rsrc_t r_a = rsrc(xq, (uint32_t)((size_t)M * K));
+    const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
+    const __amdgpu_buffer_rsrc_t r_xsum = rsrc(xsum, (PARTIALS || !AFF) ? 0u : (uint32_t)((size_t)M * ngroups * 4));
     const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, PARTIALS ? 0u : (uint32_t)((size_t)N * ngroups * 2));
     const __amdgpu_buffer_rsrc_t r_wb =
         rsrc(wbias, (PARTIALS || !AFF) ? 0u : (uint32_t)((size_t)N * ngroups * 2));
-    const uint32_t ob = (n < N) ? (uint32_t)(n * (K / 2) + 8 * (q & 1)) : OUT;  // + 16 per step
-    const uint32_t os = (n < N) ? (uint32_t)(n * ngroups * 2) : OUT;            // + 2 per group
-    uint32_t oa[MT];                                                              // + 32 per step
+
+    // Chunk staging, coalesced: consecutive threads read consecutive 16 bytes of
+    // one weight row (KC/2 bytes per row) or one activation row (KC bytes). Two
+    // register sets: the loads of chunks ch + 1 and ch + 2 are in flight while
+    // chunk ch is computed. Each lane also fetches the weight scales (and
+    // biases) of its column for the groups its wavefront will rescale.
+    constexpr int GPW = SPW / SPG;  // groups per wavefront per chunk
+    const uint32_t os = (n0 + c < N) ? (uint32_t)((n0 + c) * ngroups * 2) : OUT;  // this lane's weight-scale row
+    uint4 rw[2][W_CH], ra[2][A_CH];
+    float rxs[2][S_CH], rxb[2][S_CH];
+    uint32_t rws[2][GPW], rwb[2][GPW];
+    auto load_chunk = [&](int ch, auto setc) {
+        constexpr int B = decltype(setc)::value;
+        const int k0 = ch * KC;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) oa[t] = (16 * t + c < M) ? (uint32_t)((16 * t + c) * K + 8 * q) : OUT;
+        for (int i = 0; i < W_CH; ++i) {
+            const int idx = tid + SNT * i, r = idx / (KC / 32), seg = idx % (KC / 32);  // 16-byte segment
+            const bool in = n0 + r < N && k0 + 32 * seg < K;
+            rw[B][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                r_b, in ? (uint32_t)((n0 + r) * (K / 2) + 16 * seg) : OUT, k0 / 2, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) {
+            const int idx = tid + SNT * i, r = idx / (KC / 16), seg = idx % (KC / 16);
+            const bool in = r < M && k0 + 16 * seg < K;
+            ra[B][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                r_a, in ? (uint32_t)(r * K + 16 * seg) : OUT, k0, 0));
+        }
+        if (!PARTIALS) {
+            const int g0 = k0 / G;
+#pragma unroll
+            for (int i = 0; i < S_CH; ++i) {
+                const int idx = tid + SNT * i, r = idx / GPC, gi = idx % GPC;
+                const bool in = idx < MR * GPC && r < M && g0 + gi < ngroups;
+                const uint32_t o = in ? (uint32_t)((r * ngroups + gi) * 4) : OUT;
+                rxs[B][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, o, g0 * 4, 0));
+                rxb[B][i] = AFF ? (float)(int)__builtin_amdgcn_raw_buffer_load_b32(r_xsum, o, g0 * 4, 0) : 0.0f;
+            }
+            const int gw0 = ch * GPC + wave * GPW;
+#pragma unroll
+            for (int u = 0; u < GPW; ++u) {
+                const uint32_t o = (gw0 + u < ngroups) ? os : OUT;
+                rws[B][u] = __builtin_amdgcn_raw_buffer_load_b16(r_ws, o, (gw0 + u) * 2, 0);
+                rwb[B][u] = AFF ? __builtin_amdgcn_raw_buffer_load_b16(r_wb, o, (gw0 + u) * 2, 0) : 0u;
+            }
+        }
+    };
+    auto store_chunk = [&](auto setc) {
+        constexpr int B = decltype(setc)::value;
+#pragma unroll
+        for (int i = 0; i < W_CH; ++i) {
+            const int idx = tid + SNT * i, r = idx / (KC / 32), seg = idx % (KC / 32);
+            *reinterpret_cast<uint4*>(&S.w[r][16 * seg]) = rw[B][i];
+        }
+#pragma unroll
+        for (int i = 0; i < A_CH; ++i) {
+            const int idx = tid + SNT * i, r = idx / (KC / 16), seg = idx % (KC / 16);
+            *reinterpret_cast<uint4*>(&S.a[r][16 * seg]) = ra[B][i];
+        }
+        if (!PARTIALS) {
+#pragma unroll
+            for (int i = 0; i < S_CH; ++i) {
+                const int idx = tid + SNT * i, r = idx / GPC, gi = idx % GPC;
+                if (idx < MR * GPC) {
+                    S.xs[gi][r] = rxs[B][i];
+                    if (AFF) S.xb[gi][r] = rxs[B][i] * rxb[B][i];
+                }
+            }
+        }
+    };
+
     const int shift = 4 * (q >> 1);
 
     float acc[MT][4];
@@ -87,58 +176,29 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
 
-    constexpr int GPP = PS / SPG;  // groups per pass
-    uint2 wv[PS], av[PS][MT];
-    uint32_t wsb[GPP], wbb[GPP];
-    // issue one pass's loads; steps and groups past the range read zero
-    auto load_pass = [&](int s0) {
+    // One chunk: stage it from register set B, refill B with chunk ch + 2, compute.
+    auto do_chunk = [&](int ch, auto setc) {
+        constexpr int B = decltype(setc)::value;
+        __syncthreads();  // the previous chunk is consumed
+        store_chunk(setc);
+        uint32_t wsb[GPW], wbb[GPW];
 #pragma unroll
-        for (int p = 0; p < PS; ++p) {
-            const bool in = s0 + p < se;
-            wv[p] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r_b, in ? ob : OUT, (s0 + p) * 16, 0));
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-                av[p][t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r_a, in ? oa[t] : OUT, (s0 + p) * 32, 0));
-        }
-#pragma unroll
-        for (int u = 0; u < GPP; ++u) {
-            const int g = s0 / SPG + u;
-            const uint32_t o = (g < ge) ? os : OUT;
-            if (!PARTIALS) {
-                wsb[u] = __builtin_amdgcn_raw_buffer_load_b16(r_ws, o, g * 2, 0);
-                wbb[u] = AFF ? __builtin_amdgcn_raw_buffer_load_b16(r_wb, o, g * 2, 0) : 0u;
-            }
-        }
-    };
-
-    // The first pass's weight loads go out before the activation scales are
-    // staged, so the staging hides behind them.
-    load_pass(sb);
-    if (!PARTIALS) {
-        // rows of xs (and xsum) are read along the groups, written transposed
-        for (int i = tid; i < MR * ngroups; i += SNT) {
-            const int m = i / ngroups, g = i - m * ngroups;
-            float v = 0.0f, b = 0.0f;
-            if (m < M) {
-                v = xs[(size_t)m * ngroups + g];
-                if (AFF) b = v * (float)xsum[(size_t)m * ngroups + g];
-            }
-            sxs[g * MR + m] = v;
-            if (AFF) sxb[g * MR + m] = b;
+        for (int u = 0; u < GPW; ++u) {
+            wsb[u] = rws[B][u];
+            wbb[u] = rwb[B][u];
         }
         __syncthreads();
-    }
-
-    for (int s0 = sb; s0 < se; s0 += PS) {
-        if (s0 != sb) load_pass(s0);
+        if (ch + 2 < nchunks) load_chunk(ch + 2, setc);
+        const int gw0 = ch * GPC + wave * GPW;  // first group of this wavefront
 #pragma unroll
-        for (int u = 0; u < GPP; ++u) {
-            const int g = s0 / SPG + u;
+        for (int u = 0; u < GPW; ++u) {
+            const int g = gw0 + u;
             v4i P[MT];
 #pragma unroll
             for (int e = 0; e < SPG; ++e) {
-                const int p = u * SPG + e;
-                uint32_t lo = (wv[p].x >> shift) & 0x0F0F0F0Fu, hi = (wv[p].y >> shift) & 0x0F0F0F0Fu;
+                const int sl = wave * SPW + u * SPG + e;  // step within the chunk
+                const uint2 wv = *reinterpret_cast<const uint2*>(&S.w[c][16 * sl + 8 * (q & 1)]);
+                uint32_t lo = (wv.x >> shift) & 0x0F0F0F0Fu, hi = (wv.y >> shift) & 0x0F0F0F0Fu;
                 if (FMT == 0) {
                     lo = minus8_bytes(lo);
                     hi = minus8_bytes(hi);
@@ -146,13 +206,15 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
                 const long bop = (long)(((uint64_t)hi << 32) | lo);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
-                    const long aop = (long)(((uint64_t)av[p][t].y << 32) | av[p][t].x);
+                    const uint2 av = *reinterpret_cast<const uint2*>(&S.a[16 * t + c][32 * sl + 8 * q]);
+                    const long aop = (long)(((uint64_t)av.y << 32) | av.x);
                     const v4i z = {0, 0, 0, 0};
                     P[t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, e == 0 ? z : P[t], 0, 0, 0);
                 }
             }
             if (PARTIALS) {
-                if (g < ge && n < N) {
+                const int n = n0 + c;
+                if (g < ngroups && n < N) {
 #pragma unroll
                     for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -163,19 +225,19 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
                 }
                 continue;
             }
-            // groups past the range have zero codes and zero weight scale and bias
-            const int gs = min(g, ngroups - 1);
+            // groups past K have zero codes and zero scales and biases
+            const int gi = wave * GPW + u;  // group within the chunk
             const float w = AFF ? bf16_to_float(wsb[u]) : half_to_float(wsb[u]);
             const float b = AFF ? bf16_to_float(wbb[u]) : 0.0f;
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                const float4 xv = *reinterpret_cast<const float4*>(&sxs[gs * MR + 16 * t + 4 * q]);
+                const float4 xv = *reinterpret_cast<const float4*>(&S.xs[gi][16 * t + 4 * q]);
                 acc[t][0] += xv.x * (w * (float)P[t][0]);
                 acc[t][1] += xv.y * (w * (float)P[t][1]);
                 acc[t][2] += xv.z * (w * (float)P[t][2]);
                 acc[t][3] += xv.w * (w * (float)P[t][3]);
                 if (AFF) {
-                    const float4 bv = *reinterpret_cast<const float4*>(&sxb[gs * MR + 16 * t + 4 * q]);
+                    const float4 bv = *reinterpret_cast<const float4*>(&S.xb[gi][16 * t + 4 * q]);
                     acc[t][0] += bv.x * b;
                     acc[t][1] += bv.y * b;
                     acc[t][2] += bv.z * b;
@@ -183,20 +245,31 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
                 }
             }
         }
+    };
+
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    load_chunk(0, C0());
+    if (nchunks > 1) load_chunk(1, C1());
+    int ch = 0;
+    for (; ch + 1 < nchunks; ch += 2) {
+        do_chunk(ch, C0());
+        do_chunk(ch + 1, C1());
     }
+    if (ch < nchunks) do_chunk(ch, C0());
     if (PARTIALS) return;
 
     // combine the wavefronts' partial sums in wavefront order
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(wave * MT + t) * 256 + (4 * q + r) * 16 + c] = acc[t][r];
+        for (int r = 0; r < 4; ++r) S.red[wave][t][(4 * q + r) * 16 + c] = acc[t][r];
     __syncthreads();
     for (int o = tid; o < MT * 256; o += SNT) {
         float s = 0.0f;
 #pragma unroll
-        for (int w = 0; w < SW; ++w) s += red[w * MT * 256 + o];
-        const int m = 16 * (o >> 8) + ((o >> 4) & 15), nn = blockIdx.x * SN + (o & 15);
+        for (int w = 0; w < SW; ++w) s += S.red[w][o >> 8][o & 255];
+        const int m = 16 * (o >> 8) + ((o >> 4) & 15), nn = n0 + (o & 15);
         if (m < M && nn < N) y[(size_t)m * N + nn] = s;
     }
 }
@@ -205,13 +278,14 @@ template <int FMT, int G, int MT>
 hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                      const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                      hipStream_t stream) {
-    const size_t ngroups = (size_t)(K / G);
-    const size_t lds = partials ? 0 : (ngroups * 16 * MT * 4 * (FMT == 1 ? 2 : 1) + (size_t)SW * MT * 256 * 4);
+    const size_t lds = sizeof(SmallLds<G, MT>);
     auto k = partials ? gemm_small_kernel<FMT, G, MT, true> : gemm_small_kernel<FMT, G, MT, false>;
-    if (lds > 64 * 1024) {
+    static bool attr[2] = {false, false};
+    if (lds > 64 * 1024 && !attr[partials != nullptr]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
+        attr[partials != nullptr] = true;
     }
     hipLaunchKernelGGL(k, dim3((N + SN - 1) / SN), dim3(SNT), lds, stream, M, K, N, wq,
                        static_cast<const uint16_t*>(wscale), static_cast<const uint16_t*>(wbias), xq, xs, xsum, y,

@@ -26,11 +26,10 @@ hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, 
                        const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                        int32_t* partials, hipStream_t stream);
 
-// Few-row GEMM (1 <= M <= GEMM_SMALL_MAX_M, K <= GEMM_SMALL_MAX_K): every
-// weight block is read once for all rows (16x16x32 int8 MFMA, K split over
-// the wavefronts of a workgroup). Same arguments as launch_gemm.
+// Few-row GEMM (1 <= M <= GEMM_SMALL_MAX_M): every weight block is read once
+// for all rows (16x16x32 int8 MFMA, K chunks staged in LDS and split over the
+// wavefronts of a workgroup). Same arguments as launch_gemm.
 constexpr int GEMM_SMALL_MAX_M = 32;
-constexpr int GEMM_SMALL_MAX_K = 32768;  // activation scales of all rows staged in LDS
 hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream);

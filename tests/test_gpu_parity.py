@@ -343,7 +343,7 @@ def test_small_gemm_dispatch_boundary():
 
 @pytest.mark.parametrize("fmt,bs,M,N", [("q4_0", 32, 32, 16), ("affine", 64, 17, 20)])
 def test_small_gemm_max_k(fmt, bs, M, N):
-    # K = 32768: the activation scales of all rows fill 144 KB of LDS (Q4_0, 32 rows)
+    # K = 32768: 16 chunks of 2048 staged through LDS
     print(f"case small gemm max K {fmt} M={M} N={N}", flush=True)
     K = 32768
     wts, act = _partials_case(fmt, bs, M, K, N, 99 + M)
