@@ -305,11 +305,22 @@ def main():
         t_act = time_eager(lambda: q4.quantize_act(xt, g.bs, out=(xq, xs, xsum)), iters)
         ops = 2.0 * g.M * g.N * g.K
         act_bytes = xt.numel() * xt.element_size() + xq.numel() + 8 * xs.numel()
-        secondary[f"prefill_{name}"] = {
+        entry = {
             "gemm_us": round(t_gemm * 1e6, 2), "gemm_TOPS": round(ops / t_gemm / 1e12, 1),
             "gemm_frac_int8_peak": round(ops / t_gemm / 1e12 / INT8_PEAK_TOPS, 4),
             "act_quant_us": round(t_act * 1e6, 2), "act_quant_GB/s": round(act_bytes / t_act / 1e9, 1),
             "step_TOPS": round(ops / (t_gemm + t_act) / 1e12, 1)}
+        if g.M > 32:
+            # pre-packed weights, fused quantize + GEMM (two launches, group-major activation scales)
+            packed = q4.pack_weights(g.fmt, g.bs, gwq, gws, gwb)
+            work = torch.empty(int(q4.lib().q4_gemm_packed_work_bytes(g.M, g.K, g.bs)), dtype=torch.uint8,
+                               device=dev)
+            t_pk = time_eager(lambda: q4.gemm_packed(g.fmt, g.bs, xt, packed, g.N, y=yy, work=work), iters)
+            entry.update({"packed_step_us": round(t_pk * 1e6, 2), "packed_step_TOPS": round(ops / t_pk / 1e12, 1),
+                          "packed_gemm_us_est": round((t_pk - t_act) * 1e6, 2),
+                          "packed_gemm_frac_int8_peak_est": round(ops / (t_pk - t_act) / 1e12 / INT8_PEAK_TOPS, 4)})
+            del packed, work
+        secondary[f"prefill_{name}"] = entry
         del gwq, gws, gwb, xq, xs, xsum, yy, xt
 
     if want("q4k_gemv") or want("q4k_gemm"):

@@ -22,7 +22,9 @@ Q4_PATH_GEMV, Q4_PATH_GEMM, Q4_PATH_SMALL = 0, 1, 2
 Q4K_BLOCK_BYTES = 144
 
 EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
-           "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string")
+           "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string", "q4_packed_bytes", "q4_pack_weights",
+           "q4_gemm_packed_work_bytes", "q4_gemm_packed")
+_SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes")
 
 
 class Q4Error(RuntimeError):
@@ -53,8 +55,14 @@ def lib() -> ctypes.CDLL:
         L.q4k_gemm.argtypes = [I, I, I, P, P, P, P]
         L.q4_quantize_weights.argtypes = [I, I, I, I, I, I, P, P, P, P, P]
         L.q4k_quantize_weights.argtypes = [I, I, P, P, P]
+        L.q4_packed_bytes.argtypes = [I, I, I, I]
+        L.q4_pack_weights.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        L.q4_gemm_packed_work_bytes.argtypes = [I, I, I]
+        L.q4_gemm_packed.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
         for name in EXPORTS:
-            if name != "q4_status_string":
+            if name in _SIZE_T_FUNCS:
+                getattr(L, name).restype = ctypes.c_size_t
+            elif name != "q4_status_string":
                 getattr(L, name).restype = I
         _lib = L
     return _lib
@@ -172,6 +180,49 @@ def debug_partials(path: str, fmt: str, bs: int, wq, xq, xsum, m0: int = 0, m1: 
     _check(lib().q4_debug_partials(p, M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(xq), _ptr(xsum), m0, m1,
                                    _ptr(out), _stream(stream)), "q4_debug_partials")
     return out
+
+
+def packed_bytes(K: int, N: int, bs: int, fmt: str) -> int:
+    """Size of the packed weight buffer (0 if the arguments are invalid)."""
+    return int(lib().q4_packed_bytes(K, N, bs, _fmt(fmt)))
+
+
+def pack_weights(fmt: str, bs: int, wq, wscale, wbias, bits: int = 4, stream=None):
+    """(wq [N][K/2], wscale, wbias) -> packed uint8 buffer for gemm_packed (layout in include/q4.h)."""
+    N, Kh = wq.shape
+    K = 2 * Kh
+    nbytes = packed_bytes(K, N, bs, fmt)
+    if nbytes == 0:
+        raise ValueError("invalid shape or format for packing")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=wq.device)
+    _check(lib().q4_pack_weights(N, K, bs, _fmt(fmt), bits, _ptr(wq), _ptr(wscale), _ptr(wbias), _ptr(packed),
+                                 _stream(stream)), "q4_pack_weights")
+    return packed
+
+
+def gemm_packed(fmt: str, bs: int, x, packed, N: int, y=None, work=None, bits: int = 4, stream=None):
+    """Fused quantize + GEMM on packed weights: x [M][K] float32 / bfloat16 -> y float32 [M][N].
+    Returns (y, (xq, xs_gm, xsum_gm)): the activation codes the call used, as views of its workspace
+    (xs and xsum group-major, [K/bs][M])."""
+    M, K = x.shape
+    wbytes = int(lib().q4_gemm_packed_work_bytes(M, K, bs))
+    if wbytes == 0:
+        raise ValueError("invalid shape for the packed GEMM")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if work is None:
+        work = torch.empty(wbytes, dtype=torch.uint8, device=x.device)
+    elif work.numel() < wbytes:
+        raise ValueError(f"workspace needs {wbytes} bytes")
+    _check(lib().q4_gemm_packed(M, K, N, bs, _fmt(fmt), bits, _xdtype(x), _ptr(x), _ptr(packed), _ptr(y),
+                                _ptr(work), _stream(stream)), "q4_gemm_packed")
+    a = (M * K + 255) // 256 * 256
+    g = K // bs
+    sb = (M * g * 4 + 255) // 256 * 256
+    xq = work[:M * K].view(M, K).view(torch.int8)
+    xs = work[a:a + M * g * 4].view(torch.float32).view(g, M)
+    xsum = work[a + sb:a + sb + M * g * 4].view(torch.int32).view(g, M)
+    return y, (xq, xs, xsum)
 
 
 def q4k_gemv(blocks, x, N: int, y=None, stream=None):

@@ -8,15 +8,17 @@
 // 8-byte store. The block scale is amax / 127 in correctly rounded float32 and
 // every code is round-half-even of a correctly rounded float32 quotient
 // (act_code: a reciprocal multiply, with the exact quotient near ties).
+// GM: the scales and code sums are written group-major, [K/bs][M], which is
+// the layout the packed-weight GEMM stages with contiguous loads.
 #include "common.h"
 #include "kernels.h"
 
 namespace q4 {
 
-template <int BS, bool BF16>
+template <int BS, bool BF16, bool GM>
 __global__ __launch_bounds__(256) void quantize_act_kernel(long long nthreads, const void* __restrict__ x,
                                                            int8_t* __restrict__ xq, float* __restrict__ xs,
-                                                           int32_t* __restrict__ xsum) {
+                                                           int32_t* __restrict__ xsum, int M, int ngroups) {
     constexpr int L = BS / 8;  // lanes per block
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= nthreads) return;  // the element count is a multiple of BS: whole blocks exit together
@@ -63,32 +65,49 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(long long nthreads, c
                   ((uint32_t)(q[7] & 0xFF) << 24);
     reinterpret_cast<uint2*>(xq)[t] = make_uint2(lo, hi);
     if ((threadIdx.x & (L - 1)) == 0) {
-        const long long blk = t / L;
+        long long blk = t / L;
+        if (GM) {
+            const long long m = blk / ngroups;
+            blk = (blk - m * ngroups) * M + m;
+        }
         xs[blk] = (amax != 0.0f) ? s : 0.0f;
         xsum[blk] = sum;
     }
 }
 
-template <int BS>
-static hipError_t launch_bs(long long nthreads, bool bf16, const void* x, int8_t* xq, float* xs, int32_t* xsum,
+template <int BS, bool GM>
+static hipError_t launch_bs(int M, int K, bool bf16, const void* x, int8_t* xq, float* xs, int32_t* xsum,
                             hipStream_t stream) {
+    const long long nthreads = (long long)M * K / 8;
     const unsigned grid = (unsigned)((nthreads + 255) / 256);
     if (bf16)
-        hipLaunchKernelGGL((quantize_act_kernel<BS, true>), dim3(grid), dim3(256), 0, stream, nthreads, x, xq, xs, xsum);
+        hipLaunchKernelGGL((quantize_act_kernel<BS, true, GM>), dim3(grid), dim3(256), 0, stream, nthreads, x, xq, xs,
+                           xsum, M, K / BS);
     else
-        hipLaunchKernelGGL((quantize_act_kernel<BS, false>), dim3(grid), dim3(256), 0, stream, nthreads, x, xq, xs, xsum);
+        hipLaunchKernelGGL((quantize_act_kernel<BS, false, GM>), dim3(grid), dim3(256), 0, stream, nthreads, x, xq, xs,
+                           xsum, M, K / BS);
     return hipGetLastError();
+}
+
+template <bool GM>
+static hipError_t launch_layout(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs, int32_t* xsum,
+                                hipStream_t stream) {
+    switch (bs) {
+        case 32: return launch_bs<32, GM>(M, K, bf16, x, xq, xs, xsum, stream);
+        case 64: return launch_bs<64, GM>(M, K, bf16, x, xq, xs, xsum, stream);
+        case 128: return launch_bs<128, GM>(M, K, bf16, x, xq, xs, xsum, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_quantize_act(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs, int32_t* xsum,
                                hipStream_t stream) {
-    const long long nthreads = (long long)M * K / 8;
-    switch (bs) {
-        case 32: return launch_bs<32>(nthreads, bf16, x, xq, xs, xsum, stream);
-        case 64: return launch_bs<64>(nthreads, bf16, x, xq, xs, xsum, stream);
-        case 128: return launch_bs<128>(nthreads, bf16, x, xq, xs, xsum, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_layout<false>(M, K, bs, bf16, x, xq, xs, xsum, stream);
+}
+
+hipError_t launch_quantize_act_gm(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs,
+                                  int32_t* xsum, hipStream_t stream) {
+    return launch_layout<true>(M, K, bs, bf16, x, xq, xs, xsum, stream);
 }
 
 }  // namespace q4

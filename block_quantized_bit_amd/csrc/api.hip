@@ -34,6 +34,19 @@ int hip_status(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_ERR_HIP; }
 
 constexpr int Q4_GEMV_MAX_K = 32768;  // activation codes staged in LDS
 
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Status of a packed-weight shape: the tiled layout is addressed with 32-bit offsets.
+int packed_status(int K, int N, int bs, int fmt) {
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE) return Q4_ERR_FORMAT;
+    if (N <= 0 || K <= 0) return Q4_ERR_DIM;
+    int st = block_status(K, bs, fmt);
+    if (st) return st;
+    if (q4::packed_code_bytes(K, N) >= (1ull << 31) || q4::packed_scale_bytes(K, N, bs) >= (1ull << 31))
+        return Q4_ERR_DIM;
+    return Q4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,6 +156,47 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
     }
     return hip_status(q4::launch_gemm(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
                                       partials, s));
+}
+
+size_t q4_packed_bytes(int K, int N, int bs, int fmt) {
+    if (packed_status(K, N, bs, fmt)) return 0;
+    return q4::packed_code_bytes(K, N) + q4::packed_scale_bytes(K, N, bs) * (fmt == Q4_FMT_AFFINE ? 2 : 1);
+}
+
+int q4_pack_weights(int N, int K, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
+                    const void* wbias, uint8_t* packed, void* stream) {
+    if (bits != 4) return Q4_ERR_FORMAT;
+    int st = packed_status(K, N, bs, fmt);
+    if (st) return st;
+    if (!wq || !wscale || !packed || (fmt == Q4_FMT_AFFINE && !wbias)) return Q4_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(wscale, 2) || (wbias && !aligned(wbias, 2)) || !aligned(packed, 16))
+        return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_pack_weights(N, K, bs, fmt, wq, wscale, wbias, packed,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t q4_gemm_packed_work_bytes(int M, int K, int bs) {
+    if (M <= 0 || K <= 0 || (bs != 32 && bs != 64 && bs != 128) || K % bs != 0) return 0;
+    return align256((size_t)M * K) + 2 * align256((size_t)M * (K / bs) * 4);
+}
+
+int q4_gemm_packed(int M, int K, int N, int bs, int fmt, int bits, int xdtype, const void* x,
+                   const uint8_t* packed, float* y, void* work, void* stream) {
+    int st = matmul_status(M, K, N, bs, fmt, bits);
+    if (st) return st;
+    if (xdtype != Q4_DT_F32 && xdtype != Q4_DT_BF16) return Q4_ERR_FORMAT;
+    st = packed_status(K, N, bs, fmt);
+    if (st) return st;
+    if ((long long)M * K >= (1LL << 31)) return Q4_ERR_DIM;
+    if (!x || !packed || !y || !work) return Q4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(y, 4) || !aligned(work, 16)) return Q4_ERR_ALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int8_t* xq = static_cast<int8_t*>(work);
+    float* xs = reinterpret_cast<float*>(static_cast<uint8_t*>(work) + align256((size_t)M * K));
+    int32_t* xsum = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(xs) + align256((size_t)M * (K / bs) * 4));
+    st = hip_status(q4::launch_quantize_act_gm(M, K, bs, xdtype == Q4_DT_BF16, x, xq, xs, xsum, s));
+    if (st) return st;
+    return hip_status(q4::launch_gemm_packed(M, K, N, bs, fmt, packed, xq, xs, xsum, y, s));
 }
 
 int q4k_gemv(int M, int K, int N, const void* blocks, const float* x, float* y, void* stream) {

@@ -104,7 +104,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
 }
 
-template <int FMT, int G, bool PARTIALS>
+// PACKED: wq, wscale and wbias point into a packed weight buffer (one 8 KB
+// block of codes per 128-column tile and stage, rows in order; scales and
+// biases as [tile][group][128]) and xs, xsum are group-major, [K/G][M]. Every
+// staging load of the stage is then contiguous across the workgroup's threads.
+template <int FMT, int G, bool PARTIALS, bool PACKED>
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
                                                       const uint16_t* __restrict__ wscale,
                                                       const uint16_t* __restrict__ wbias,
@@ -133,12 +137,14 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
 
     // ---------------------------------------------------------------- staging
     const __amdgpu_buffer_rsrc_t r_a = rsrc(xq, (uint32_t)((size_t)M * K));
-    const __amdgpu_buffer_rsrc_t r_b = rsrc(wq, (uint32_t)((size_t)N * (K / 2)));
+    const int ntn = (N + BN - 1) / BN;  // column tiles
+    const size_t wrows = PACKED ? (size_t)ntn * BN : (size_t)N;  // weight rows as stored
+    const __amdgpu_buffer_rsrc_t r_b =
+        rsrc(wq, (uint32_t)(PACKED ? (size_t)ntn * nstages * (BN * KS / 2) : (size_t)N * (K / 2)));
     const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
     const __amdgpu_buffer_rsrc_t r_xsum = rsrc(xsum, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
-    const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, PARTIALS ? 0u : (uint32_t)((size_t)N * ngroups * 2));
-    const __amdgpu_buffer_rsrc_t r_wb =
-        rsrc(wbias, (PARTIALS || !AFF) ? 0u : (uint32_t)((size_t)N * ngroups * 2));
+    const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, PARTIALS ? 0u : (uint32_t)(wrows * ngroups * 2));
+    const __amdgpu_buffer_rsrc_t r_wb = rsrc(wbias, (PARTIALS || !AFF) ? 0u : (uint32_t)(wrows * ngroups * 2));
     constexpr uint32_t OUT = 0x80000000u;  // beyond every buffer range: reads as zero
 
     // per-lane offsets, fixed for the whole kernel (each stage adds a scalar offset)
@@ -151,7 +157,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
         const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
-        off_b[i] = (n0 + c < N) ? (uint32_t)((n0 + c) * (K / 2) + b * 16) : OUT;
+        // packed: row c's 64 bytes of the stage sit at c * 64 of the tile's block
+        off_b[i] = PACKED ? (uint32_t)(idx * 16) : (n0 + c < N) ? (uint32_t)((n0 + c) * (K / 2) + b * 16) : OUT;
     }
     // scale staging: the thread covers (gi, r) = divmod(tid + NT*i, 128) of the
     // GPS*128 activation scales and of the GPS*128 weight scales
@@ -163,8 +170,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     for (int i = 0; i < SC_N; ++i) {
         const int idx = tid + NT * i, gi = idx / BM, r = idx % BM;
         const bool used = idx < GPS * BM;
-        off_xs[i] = (used && m0 + r < M) ? (uint32_t)(((m0 + r) * ngroups + gi) * 4) : OUT;
-        off_ws[i] = (used && n0 + r < N) ? (uint32_t)(((n0 + r) * ngroups + gi) * 2) : OUT;
+        if (PACKED) {
+            off_xs[i] = (used && m0 + r < M) ? (uint32_t)((gi * M + m0 + r) * 4) : OUT;
+            off_ws[i] = used ? (uint32_t)((gi * BN + r) * 2) : OUT;
+        } else {
+            off_xs[i] = (used && m0 + r < M) ? (uint32_t)(((m0 + r) * ngroups + gi) * 4) : OUT;
+            off_ws[i] = (used && n0 + r < N) ? (uint32_t)(((n0 + r) * ngroups + gi) * 2) : OUT;
+        }
     }
 
     uint4 ra[A_CH], rb[B_CH];
@@ -189,19 +201,22 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
         for (int i = 0; i < B_CH; ++i) {
             const int b = (tid + NT * i) & 3;
             const uint32_t o = (b * 32 < ks) ? off_b[i] : OUT;
-            rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_b, o, k0 >> 1, 0));
+            const int sb = PACKED ? (tn * nstages + st) * (BN * KS / 2) : (k0 >> 1);
+            rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_b, o, sb, 0));
         }
         if (!PARTIALS) {
             const int g0 = k0 / G;
+            const int sx = PACKED ? g0 * M * 4 : g0 * 4;
+            const int sw = PACKED ? (tn * ngroups + g0) * (BN * 2) : g0 * 2;
 #pragma unroll
             for (int i = 0; i < SC_N; ++i) {
                 const int gi = (tid + NT * i) / BM;
                 const bool in = gi * G < ks;
                 const uint32_t ox = in ? off_xs[i] : OUT, ow = in ? off_ws[i] : OUT;
-                rxs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, ox, g0 * 4, 0));
-                if (AFF) rxsum[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r_xsum, ox, g0 * 4, 0);
-                rws[i] = __builtin_amdgcn_raw_buffer_load_b16(r_ws, ow, g0 * 2, 0);
-                if (AFF) rwb[i] = __builtin_amdgcn_raw_buffer_load_b16(r_wb, ow, g0 * 2, 0);
+                rxs[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, ox, sx, 0));
+                if (AFF) rxsum[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r_xsum, ox, sx, 0);
+                rws[i] = __builtin_amdgcn_raw_buffer_load_b16(r_ws, ow, sw, 0);
+                if (AFF) rwb[i] = __builtin_amdgcn_raw_buffer_load_b16(r_wb, ow, sw, 0);
             }
         }
     };
@@ -424,7 +439,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     }
 }
 
-template <int FMT, int G>
+template <int FMT, int G, bool PACKED>
 hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                       hipStream_t stream) {
@@ -432,7 +447,7 @@ hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale
     const size_t lds = 2 * sizeof(Tiles) + RING * sizeof(Scales<G, FMT>);
     const uint16_t* ws = static_cast<const uint16_t*>(wscale);
     const uint16_t* wb = static_cast<const uint16_t*>(wbias);
-    auto k = partials ? gemm_kernel<FMT, G, true> : gemm_kernel<FMT, G, false>;
+    auto k = partials ? gemm_kernel<FMT, G, true, PACKED> : gemm_kernel<FMT, G, false, PACKED>;
     static bool attr[2] = {false, false};
     if (!attr[partials != nullptr]) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -443,14 +458,76 @@ hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale
     return hipGetLastError();
 }
 
+// Packed weights: copy row r's bytes of stage s into block (t, s) and the
+// scales (and biases) into [tile][group][128]; rows past N are zero, so the
+// GEMM's staging of a packed tile needs no row masks.
+__global__ __launch_bounds__(256) void pack_codes_kernel(int N, int K, const uint8_t* __restrict__ wq,
+                                                         uint8_t* __restrict__ out, long long nchunks) {
+    const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // 16-byte chunk of the output
+    if (j >= nchunks) return;
+    const int nstages = (K + KS - 1) / KS;
+    const long long blk = j / (BN * KS / 32);
+    const int within = (int)(j - blk * (BN * KS / 32));
+    const int t = (int)(blk / nstages), st = (int)(blk - (long long)t * nstages);
+    const int r = within >> 2, b = within & 3;
+    const int n = t * BN + r, kb = st * (KS / 2) + 16 * b;  // byte offset in the row
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N && kb < K / 2) v = *reinterpret_cast<const uint4*>(wq + (size_t)n * (K / 2) + kb);
+    reinterpret_cast<uint4*>(out)[j] = v;
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(int N, int ngroups, const uint16_t* __restrict__ ws,
+                                                          uint16_t* __restrict__ out, long long count) {
+    const long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // (tile, group, row)
+    if (j >= count) return;
+    const int r = (int)(j % BN);
+    const long long tg = j / BN;
+    const int g = (int)(tg % ngroups), t = (int)(tg / ngroups);
+    const int n = t * BN + r;
+    out[j] = (n < N) ? ws[(size_t)n * ngroups + g] : (uint16_t)0;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
                        const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                        int32_t* partials, hipStream_t stream) {
-    if (fmt == 0) return launch_fmt<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (bs == 64) return launch_fmt<1, 64>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (bs == 128) return launch_fmt<1, 128>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (fmt == 0) return launch_fmt<0, 32, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bs == 64) return launch_fmt<1, 64, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bs == 128) return launch_fmt<1, 128, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return hipErrorInvalidValue;
+}
+
+size_t packed_code_bytes(int K, int N) {
+    return (size_t)((N + BN - 1) / BN) * ((K + KS - 1) / KS) * (BN * KS / 2);
+}
+
+size_t packed_scale_bytes(int K, int N, int bs) { return (size_t)((N + BN - 1) / BN) * (K / bs) * BN * 2; }
+
+hipError_t launch_pack_weights(int N, int K, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                               const void* wbias, uint8_t* packed, hipStream_t stream) {
+    const size_t cb = packed_code_bytes(K, N), sb = packed_scale_bytes(K, N, bs);
+    const long long nchunks = (long long)(cb / 16);
+    hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, stream, N, K, wq,
+                       packed, nchunks);
+    const long long count = (long long)(sb / 2);
+    const unsigned grid = (unsigned)((count + 255) / 256);
+    hipLaunchKernelGGL(pack_scales_kernel, dim3(grid), dim3(256), 0, stream, N, K / bs,
+                       static_cast<const uint16_t*>(wscale), reinterpret_cast<uint16_t*>(packed + cb), count);
+    if (fmt == 1)
+        hipLaunchKernelGGL(pack_scales_kernel, dim3(grid), dim3(256), 0, stream, N, K / bs,
+                           static_cast<const uint16_t*>(wbias), reinterpret_cast<uint16_t*>(packed + cb + sb), count);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_packed(int M, int K, int N, int bs, int fmt, const uint8_t* packed, const int8_t* xq,
+                              const float* xs_gm, const int32_t* xsum_gm, float* y, hipStream_t stream) {
+    const size_t cb = packed_code_bytes(K, N), sb = packed_scale_bytes(K, N, bs);
+    const void* ws = packed + cb;
+    const void* wb = packed + cb + sb;
+    if (fmt == 0) return launch_fmt<0, 32, true>(M, K, N, packed, ws, nullptr, xq, xs_gm, xsum_gm, y, nullptr, stream);
+    if (bs == 64) return launch_fmt<1, 64, true>(M, K, N, packed, ws, wb, xq, xs_gm, xsum_gm, y, nullptr, stream);
+    if (bs == 128) return launch_fmt<1, 128, true>(M, K, N, packed, ws, wb, xq, xs_gm, xsum_gm, y, nullptr, stream);
     return hipErrorInvalidValue;
 }
 

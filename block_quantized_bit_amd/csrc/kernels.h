@@ -9,6 +9,9 @@ namespace q4 {
 
 hipError_t launch_quantize_act(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs,
                                int32_t* xsum, hipStream_t stream);
+// Same codes, with xs and xsum written group-major: [K/bs][M].
+hipError_t launch_quantize_act_gm(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs,
+                                  int32_t* xsum, hipStream_t stream);
 
 // fmt: 0 = Q4_0 (bs 32), 1 = affine (bs 64 / 128). partials != nullptr selects
 // the integer-partials store in place of the float epilogue.
@@ -33,6 +36,15 @@ constexpr int GEMM_SMALL_MAX_M = 32;
 hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream);
+
+// Packed weights for the tiled GEMM (layout in include/q4.h, q4_pack_weights).
+size_t packed_code_bytes(int K, int N);
+size_t packed_scale_bytes(int K, int N, int bs);
+hipError_t launch_pack_weights(int N, int K, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                               const void* wbias, uint8_t* packed, hipStream_t stream);
+// Tiled GEMM on packed weights with group-major activation scales ([K/bs][M]).
+hipError_t launch_gemm_packed(int M, int K, int N, int bs, int fmt, const uint8_t* packed, const int8_t* xq,
+                              const float* xs_gm, const int32_t* xsum_gm, float* y, hipStream_t stream);
 
 hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
 hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);

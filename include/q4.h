@@ -53,6 +53,7 @@
 #ifndef Q4_H
 #define Q4_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -190,6 +191,43 @@ int q4_quantize_weights(int N, int K, int bs, int fmt, int bits, int wdtype,
                         const void* w, uint8_t* wq, void* wscale, void* wbias,
                         void* stream);
 int q4k_quantize_weights(int N, int K, const float* w, void* blocks, void* stream);
+
+/*
+ * Weight pre-pack for the tiled GEMM, and the fused quantize + GEMM on packed
+ * weights (tract PR #2432, production direction: a pre-packed weight layout
+ * and fusing the activation quantization into the matmul remove per-call
+ * overhead). The arithmetic is that of q4_quantize_act followed by q4_gemm.
+ *
+ * Packed layout, T = ceil(N/128) column tiles, S = ceil(K/128) K stages,
+ * ng = K/bs groups, three sections back to back:
+ *   codes   T*S blocks of 8192 bytes; block (t, s) holds, for r = 0..127 at
+ *           offset 64*r, bytes 64*s .. 64*s + 63 of row 128*t + r of wq (the
+ *           codes of that row's weights 128*s .. 128*s + 127); rows past N
+ *           and bytes past K/2 are zero.
+ *   scales  T*ng*128 16-bit values, (t, g, r) at index (t*ng + g)*128 + r:
+ *           wscale[128*t + r][g], zero for rows past N.
+ *   biases  (affine only) the same from wbias.
+ * q4_packed_bytes returns the size (0 for invalid arguments; the code and
+ * scale sections must each be below 2^31 bytes). q4_pack_weights writes the
+ * packed buffer (16-byte aligned, caller-owned) from wq, wscale, wbias as
+ * q4_quantize_weights makes them.
+ *
+ * q4_gemm_packed: x [M][K] float32 or bfloat16 (xdtype, 16-byte aligned),
+ * packed as above, y [M][N] float32. work: caller-owned scratch of
+ * q4_gemm_packed_work_bytes(M, K, bs) bytes (16-byte aligned). After the
+ * stream completes, work holds the activation codes used: xq [M][K] at
+ * offset 0, then at offset A = align256(M*K) xs as [K/bs][M] float32
+ * (group-major, the transpose of q4_quantize_act's xs), then at offset
+ * A + align256(4*M*K/bs) xsum as [K/bs][M] int32. Two launches on stream:
+ * the quantizer, then the tiled 32x32x32 int8 MFMA GEMM (for every M).
+ * M*K must be below 2^31.
+ */
+size_t q4_packed_bytes(int K, int N, int bs, int fmt);
+int q4_pack_weights(int N, int K, int bs, int fmt, int bits, const uint8_t* wq,
+                    const void* wscale, const void* wbias, uint8_t* packed, void* stream);
+size_t q4_gemm_packed_work_bytes(int M, int K, int bs);
+int q4_gemm_packed(int M, int K, int N, int bs, int fmt, int bits, int xdtype, const void* x,
+                   const uint8_t* packed, float* y, void* work, void* stream);
 
 /* Static name of a q4_status value ("unknown status" otherwise). */
 const char* q4_status_string(int status);

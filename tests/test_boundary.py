@@ -23,13 +23,13 @@ MIS = 0x100001
 
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "q4.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(q4k?_\w+)\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(q4k?_\w+)\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 14
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None
@@ -116,6 +116,37 @@ def test_debug_partials_validation():
     # few-row kernel: at most 32 rows
     big = [2, 40, 128, 8, 32, 0, 4, A, A, A, 0, 33, A, None]
     assert f(*big) == RANGE
+
+
+def test_packed_sizes_and_validation():
+    L = q4.lib()
+    # 4096 x 14336, g128: 112 column tiles x 32 stages x 8 KB codes, 112 x 32 x 128 bf16 scales and biases
+    assert L.q4_packed_bytes(4096, 14336, 128, 1) == 112 * 32 * 8192 + 2 * 112 * 32 * 256
+    # ragged: N = 130 -> 2 tiles, K = 160 -> 2 stages, 5 groups of 32
+    assert L.q4_packed_bytes(160, 130, 32, 0) == 2 * 2 * 8192 + 2 * 5 * 256
+    assert L.q4_packed_bytes(160, 130, 32, 2) == 0
+    assert L.q4_packed_bytes(100, 130, 32, 0) == 0
+    assert L.q4_packed_bytes(160, 0, 32, 0) == 0
+    assert L.q4_gemm_packed_work_bytes(3, 160, 32) == 512 + 2 * 256
+    assert L.q4_gemm_packed_work_bytes(3, 100, 32) == 0
+    p = L.q4_pack_weights
+    assert p(8, 128, 32, 0, 8, A, A, None, A, None) == FORMAT
+    assert p(8, 128, 64, 1, 4, A, A, None, A, None) == NULL
+    assert p(8, 128, 32, 0, 4, A, A, None, None, None) == NULL
+    assert p(8, 128, 32, 0, 4, A, A, None, A + 8, None) == ALIGN
+    assert p(8, 100, 32, 0, 4, A, A, None, A, None) == BLOCK
+    g = L.q4_gemm_packed
+    base = [4, 128, 8, 32, 0, 4, 0, A, A, A, A, None]
+    args = list(base); args[6] = 5
+    assert g(*args) == FORMAT
+    args = list(base); args[5] = 6
+    assert g(*args) == FORMAT
+    args = list(base); args[10] = None
+    assert g(*args) == NULL
+    args = list(base); args[10] = A + 4
+    assert g(*args) == ALIGN
+    args = list(base); args[0] = 0
+    assert g(*args) == DIM
 
 
 def test_q4k_validation():

@@ -377,6 +377,87 @@ def test_small_gemm_deterministic():
     assert torch.equal(y1, y2)
 
 
+# ---------------------------------------------------------------- packed weights, fused quantize + GEMM
+
+def _pack_reference(wq, ws, wb, K, N, bs):
+    """The packed layout of include/q4.h written out with numpy reshapes."""
+    T, S, ng = -(-N // 128), -(-K // 128), K // bs
+    wpad = np.zeros((T * 128, S * 64), np.uint8)
+    wpad[:N, :K // 2] = wq
+    codes = wpad.reshape(T, 128, S, 64).transpose(0, 2, 1, 3)      # [t][s][r][64 bytes]
+    parts = [np.ascontiguousarray(codes).tobytes()]
+    for a in (ws, wb):
+        if a is None:
+            continue
+        pad = np.zeros((T * 128, ng), np.uint16)
+        pad[:N] = a
+        parts.append(np.ascontiguousarray(pad.reshape(T, 128, ng).transpose(0, 2, 1)).tobytes())  # [t][g][r]
+    return np.frombuffer(b"".join(parts), dtype=np.uint8)
+
+
+PACK_CASES = [("q4_0", 32, 3, 160, 130), ("q4_0", 32, 130, 416, 257), ("affine", 64, 65, 320, 129),
+              ("affine", 128, 200, 384, 131), ("affine", 128, 33, 1152, 256)]
+
+
+@pytest.mark.parametrize("fmt,bs,M,K,N", PACK_CASES)
+def test_pack_weights_layout(fmt, bs, M, K, N):
+    print(f"case pack {fmt} bs={bs} K={K} N={N}", flush=True)
+    wts, _ = _partials_case(fmt, bs, 1, K, N, 11 * K + N)
+    g = _wts_dev(fmt, wts)
+    packed = q4.pack_weights(fmt, bs, *g)
+    _sync()
+    ref = _pack_reference(wts[0], wts[1], wts[2] if fmt == "affine" else None, K, N, bs)
+    assert packed.numel() == ref.size == q4.packed_bytes(K, N, bs, fmt)
+    assert np.array_equal(to_np(packed), ref)
+
+
+@pytest.mark.parametrize("fmt,bs,M,K,N", PACK_CASES)
+def test_gemm_packed_ragged(fmt, bs, M, K, N):
+    print(f"case gemm packed {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(13 * M + K + N)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if fmt == "affine":
+        x = synth.bf16_bits(x)
+        xd = to_dev(x, torch.bfloat16)
+    else:
+        xd = to_dev(x)
+    wts, _ = _partials_case(fmt, bs, 1, K, N, 17 * K + N)
+    g = _wts_dev(fmt, wts)
+    packed = q4.pack_weights(fmt, bs, *g)
+    y, (xq, xs_gm, xsum_gm) = q4.gemm_packed(fmt, bs, xd, packed, N)
+    _sync()
+    act = oracle.quantize_act(x, bs)
+    # the codes the call used: bit-identical to the quantizer's, scales transposed
+    assert np.array_equal(to_np(xq), act[0])
+    assert np.array_equal(to_np(xs_gm).T.view(np.uint32), act[1].view(np.uint32))
+    assert np.array_equal(to_np(xsum_gm).T, act[2])
+    assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+    if M > 32:
+        # same tiled kernel arithmetic as the unpacked GEMM: identical results
+        yu = q4.gemm(fmt, bs, *g, xq, *[to_dev(a) for a in act[1:]])
+        _sync()
+        assert torch.equal(y, yu)
+
+
+@pytest.mark.parametrize("name", ["affine_g128_4096x4096x14336", "affine_g128_4096x14336x4096"])
+def test_gemm_packed_workload_sampled(name):
+    print(f"case gemm packed sampled {name}", flush=True)
+    wl, x, _, _, wts = workload_data(name)
+    g = _wts_dev(wl.fmt, wts)
+    packed = q4.pack_weights(wl.fmt, wl.bs, *g)
+    xd = to_dev(x)
+    y, (xq, xs_gm, xsum_gm) = q4.gemm_packed(wl.fmt, wl.bs, xd, packed, wl.N)
+    gq, gs, gsum = q4.quantize_act(xd, wl.bs)
+    yu = q4.gemm(wl.fmt, wl.bs, *g, gq, gs, gsum)
+    _sync()
+    assert torch.equal(xq, gq) and torch.equal(xs_gm.t(), gs) and torch.equal(xsum_gm.t(), gsum)
+    assert torch.equal(y, yu)
+    act = (to_np(gq), to_np(gs), to_np(gsum))
+    ms, ns = sample_pairs(wl.M, wl.N, 1000, wl.K + 7)
+    ref = _oracle_y_sample(wl.fmt, wts, act, wl.K, wl.N, wl.bs, ms, ns)
+    assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
+
+
 # ---------------------------------------------------------------- Q4_K
 
 def test_q4k_gemv_workload():
