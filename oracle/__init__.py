@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.or_q4k_gemv.argtypes = [I, I, P, P, P]
         L.or_q4k_gemm.argtypes = [I, I, I, P, P, P]
         L.or_q4k_gemm_sample.argtypes = [I, I, I, P, P, I, P, P, P]
+        L.or_q4k_backward.argtypes = [I, I, I, P, P, P]
+        L.or_q4_backward.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        L.or_q4k_backward_sample.argtypes = [I, I, I, P, P, I, P, P, P]
+        L.or_q4_backward_sample.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, P]
         _lib = L
     return _lib
 
@@ -262,3 +266,50 @@ def q4k_gemm_sample(blocks, x, K: int, N: int, ms, ns) -> np.ndarray:
     _ok(lib().or_q4k_gemm_sample(x.shape[0], K, N, _p(blocks), _p(x), ms.shape[0], _p(ms),
                                  _p(ns), _p(y)), "q4k_gemm_sample")
     return y
+
+
+# ---- input gradient with frozen weights ---------------------------------------
+
+def q4k_backward(blocks, dy, K: int, N: int) -> np.ndarray:
+    """dx [M][K] = dy [M][N] . dequant(W) (C-Kernel-Engine backward pass: W^T . dY per row)."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    M = dy.shape[0]
+    dx = np.empty((M, K), dtype=np.float32)
+    _ok(lib().or_q4k_backward(M, K, N, _p(blocks), _p(dy), _p(dx)), "q4k_backward")
+    return dx
+
+
+def q4_backward(wq, wscale, wbias, dy, K: int, N: int, bs: int, fmt: int) -> np.ndarray:
+    """dx [M][K] = dy [M][N] . dequant(W) for Q4_0 / affine weights."""
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    ws, wb = _scales(wscale, wbias)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    M = dy.shape[0]
+    dx = np.empty((M, K), dtype=np.float32)
+    _ok(lib().or_q4_backward(M, K, N, bs, fmt, _p(wq), _p(ws), None if wb is None else _p(wb), _p(dy), _p(dx)),
+        "q4_backward")
+    return dx
+
+
+def q4k_backward_sample(blocks, dy, K: int, N: int, ms, ks) -> np.ndarray:
+    blocks = np.ascontiguousarray(blocks, dtype=np.uint8)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    ms = np.ascontiguousarray(ms, dtype=np.int32)
+    ks = np.ascontiguousarray(ks, dtype=np.int32)
+    dx = np.empty(ms.shape[0], dtype=np.float32)
+    _ok(lib().or_q4k_backward_sample(dy.shape[0], K, N, _p(blocks), _p(dy), ms.shape[0], _p(ms), _p(ks), _p(dx)),
+        "q4k_backward_sample")
+    return dx
+
+
+def q4_backward_sample(wq, wscale, wbias, dy, K: int, N: int, bs: int, fmt: int, ms, ks) -> np.ndarray:
+    wq = np.ascontiguousarray(wq, dtype=np.uint8)
+    ws, wb = _scales(wscale, wbias)
+    dy = np.ascontiguousarray(dy, dtype=np.float32)
+    ms = np.ascontiguousarray(ms, dtype=np.int32)
+    ks = np.ascontiguousarray(ks, dtype=np.int32)
+    dx = np.empty(ms.shape[0], dtype=np.float32)
+    _ok(lib().or_q4_backward_sample(dy.shape[0], K, N, bs, fmt, _p(wq), _p(ws), None if wb is None else _p(wb),
+                                    _p(dy), ms.shape[0], _p(ms), _p(ks), _p(dx)), "q4_backward_sample")
+    return dx

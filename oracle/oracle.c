@@ -514,3 +514,93 @@ int or_q4k_gemm_sample(int M, int K, int N, const uint8_t* blocks, const float* 
     }
     return OR_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Input gradient with frozen weights ([cke] section "Backward Pass:         */
+/* Gradient w.r.t. Input": dL/dX = W^T . dL/dY with the weights dequantized  */
+/* on the fly and no weight gradient; its batched form is one such product   */
+/* per activation row).                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Dequantized Q4_0 or affine weight (n, k), exact in double. */
+static double w4_weight(int K, int bs, int fmt, const uint8_t* wq, const uint16_t* wscale,
+                        const uint16_t* wbias, long n, int k) {
+    int nb = K / bs, b = k / bs;
+    int q = get_code(wq + n * (long)(K / 2), k);
+    if (fmt == 0) return (double)or_f16_to_f32(wscale[n * nb + b]) * (double)(q - 8);
+    return (double)or_bf16_to_f32(wscale[n * nb + b]) * (double)q + (double)or_bf16_to_f32(wbias[n * nb + b]);
+}
+
+/* dx[m][k] = sum_n dy[m][n] * w^[n][k]: every term exact in double, summed in
+ * n order, rounded once to float. dy [M][N], dx [M][K] float32. The weights
+ * are dequantized one row at a time (w_row), each row once. */
+static int backward_rows(int M, int K, int N, const float* dy, float* dx,
+                         double (*weight)(const void* ctx, long n, int k), const void* ctx) {
+    double* acc = (double*)calloc((size_t)M * K + 1, sizeof(double));
+    double* w_row = (double*)malloc(((size_t)K + 1) * sizeof(double));
+    if (!acc || !w_row) { free(acc); free(w_row); return OR_BAD; }
+    for (long n = 0; n < N; ++n) {
+        for (int k = 0; k < K; ++k) w_row[k] = weight(ctx, n, k);
+        for (long m = 0; m < M; ++m) {
+            double g = (double)dy[m * (long)N + n];
+            for (int k = 0; k < K; ++k) acc[m * (long)K + k] += g * w_row[k];
+        }
+    }
+    for (long i = 0; i < (long)M * K; ++i) dx[i] = (float)acc[i];
+    free(acc);
+    free(w_row);
+    return OR_OK;
+}
+
+struct q4k_ctx { int K; const uint8_t* blocks; };
+static double q4k_ctx_weight(const void* c, long n, int k) {
+    const struct q4k_ctx* x = (const struct q4k_ctx*)c;
+    int nb = x->K / QK;
+    return q4k_weight(x->blocks + (n * nb + k / QK) * (long)Q4K_BYTES, k % QK);
+}
+
+struct w4_ctx { int K, bs, fmt; const uint8_t* wq; const uint16_t* ws; const uint16_t* wb; };
+static double w4_ctx_weight(const void* c, long n, int k) {
+    const struct w4_ctx* x = (const struct w4_ctx*)c;
+    return w4_weight(x->K, x->bs, x->fmt, x->wq, x->ws, x->wb, n, k);
+}
+
+int or_q4k_backward(int M, int K, int N, const uint8_t* blocks, const float* dy, float* dx) {
+    if (M < 0 || N < 0 || K <= 0 || K % QK != 0) return OR_BAD;
+    struct q4k_ctx c = {K, blocks};
+    return backward_rows(M, K, N, dy, dx, q4k_ctx_weight, &c);
+}
+
+int or_q4_backward(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const uint16_t* wscale,
+                   const uint16_t* wbias, const float* dy, float* dx) {
+    if (check_fmt(K, bs, fmt) || M < 0 || N < 0) return OR_BAD;
+    struct w4_ctx c = {K, bs, fmt, wq, wscale, wbias};
+    return backward_rows(M, K, N, dy, dx, w4_ctx_weight, &c);
+}
+
+/* dx for the listed (ms[i], ks[i]) only, same arithmetic. */
+static int backward_sample(int M, int K, int N, const float* dy, int count, const int* ms, const int* ks,
+                           float* dx, double (*weight)(const void* ctx, long n, int k), const void* ctx) {
+    for (int i = 0; i < count; ++i) {
+        if (ms[i] < 0 || ms[i] >= M || ks[i] < 0 || ks[i] >= K) return OR_BAD;
+        double acc = 0.0;
+        for (long n = 0; n < N; ++n) acc += (double)dy[ms[i] * (long)N + n] * weight(ctx, n, ks[i]);
+        dx[i] = (float)acc;
+    }
+    return OR_OK;
+}
+
+int or_q4k_backward_sample(int M, int K, int N, const uint8_t* blocks, const float* dy, int count,
+                           const int* ms, const int* ks, float* dx) {
+    if (K <= 0 || K % QK != 0) return OR_BAD;
+    struct q4k_ctx c = {K, blocks};
+    return backward_sample(M, K, N, dy, count, ms, ks, dx, q4k_ctx_weight, &c);
+}
+
+int or_q4_backward_sample(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const uint16_t* wscale,
+                          const uint16_t* wbias, const float* dy, int count, const int* ms, const int* ks,
+                          float* dx) {
+    if (check_fmt(K, bs, fmt)) return OR_BAD;
+    struct w4_ctx c = {K, bs, fmt, wq, wscale, wbias};
+    return backward_sample(M, K, N, dy, count, ms, ks, dx, w4_ctx_weight, &c);
+}
