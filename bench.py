@@ -48,7 +48,7 @@ def parse_args():
     p.add_argument("--only", default=None,
                    help="run one workload alone (for profiling): gemv_fused (eager decode launches, --steps of "
                         "them), gemm_3a, gemm_3b, gemm_2, gemm_0, q4k_gemv, q4k_gemm, act_quant, gemv_plain, "
-                        "small_m")
+                        "small_m, q4k_backward, q4_backward")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run a plain device-to-device copy of this many MiB (counter calibration) and exit")
     return p.parse_args()
@@ -361,6 +361,43 @@ def main():
             secondary["q4k_gemm_16x4096x14336"] = {
                 "us": round(t * 1e6, 2), "TFLOPS": round(flops / t / 1e12, 2),
                 "frac_fp32_peak": round(flops / t / 1e12 / FP32_PEAK_TFLOPS, 4), "GB/s": round(qbytes / t / 1e9, 1)}
+
+    if want("q4k_backward") or want("q4_backward"):
+        # input gradient with frozen weights, dx [M][4096] = dy [M][14336] . dequant(W), 8 rotating weight copies
+        g1 = synth.workload("q4_k_gemv_1x4096x14336")
+        w4 = torch.from_numpy(synth.gen.weights(g1)).to(dev)
+        out = {}
+        if want("q4k_backward"):
+            blocks = q4.q4k_quantize_weights(w4)
+            wcopies = [blocks.clone() for _ in range(8)]
+            wbytes = blocks.numel()
+            for M in (1, 16):
+                dyt = torch.randn((M, g1.N), generator=torch.Generator(device="cpu").manual_seed(M)).to(dev)
+                dxt = torch.empty((M, g1.K), dtype=torch.float32, device=dev)
+                work = torch.empty(int(q4.lib().q4_backward_work_bytes(M, g1.K, g1.N)) // 4, dtype=torch.float32,
+                                   device=dev)
+                it = [0]
+
+                def bw():
+                    q4.q4k_gemm_backward(wcopies[it[0] % 8], dyt, g1.K, dx=dxt, work=work)
+                    it[0] += 1
+                t = time_eager(bw, 64)
+                out[f"q4k_{M}x4096x14336"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(wbytes / t / 1e9, 1),
+                                              "TFLOPS": round(2.0 * M * g1.K * g1.N / t / 1e12, 2)}
+            del wcopies, blocks
+        if want("q4_backward"):
+            wq, wd, _ = q4.quantize_weights(w4, "q4_0", 32)
+            wbytes = wq.numel() + 2 * wd.numel()
+            for M in (1, 16):
+                dyt = torch.randn((M, g1.N), generator=torch.Generator(device="cpu").manual_seed(M)).to(dev)
+                dxt = torch.empty((M, g1.K), dtype=torch.float32, device=dev)
+                work = torch.empty(int(q4.lib().q4_backward_work_bytes(M, g1.K, g1.N)) // 4, dtype=torch.float32,
+                                   device=dev)
+                t = time_eager(lambda: q4.gemm_backward("q4_0", 32, wq, wd, None, dyt, dx=dxt, work=work), 64)
+                out[f"q4_0_{M}x4096x14336"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(wbytes / t / 1e9, 1),
+                                               "TFLOPS": round(2.0 * M * g1.K * g1.N / t / 1e12, 2)}
+        secondary["input_gradient_frozen_weights"] = out
+        del w4
 
     if secondary:
         result["secondary"] = secondary

@@ -23,8 +23,9 @@ Q4K_BLOCK_BYTES = 144
 
 EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
            "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string", "q4_packed_bytes", "q4_pack_weights",
-           "q4_gemm_packed_work_bytes", "q4_gemm_packed")
-_SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes")
+           "q4_gemm_packed_work_bytes", "q4_gemm_packed", "q4_backward_work_bytes", "q4k_gemm_backward",
+           "q4_gemm_backward")
+_SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes", "q4_backward_work_bytes")
 
 
 class Q4Error(RuntimeError):
@@ -59,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.q4_pack_weights.argtypes = [I, I, I, I, I, P, P, P, P, P]
         L.q4_gemm_packed_work_bytes.argtypes = [I, I, I]
         L.q4_gemm_packed.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P]
+        L.q4_backward_work_bytes.argtypes = [I, I, I]
+        L.q4k_gemm_backward.argtypes = [I, I, I, P, P, P, P, P]
+        L.q4_gemm_backward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
         for name in EXPORTS:
             if name in _SIZE_T_FUNCS:
                 getattr(L, name).restype = ctypes.c_size_t
@@ -223,6 +227,40 @@ def gemm_packed(fmt: str, bs: int, x, packed, N: int, y=None, work=None, bits: i
     xs = work[a:a + M * g * 4].view(torch.float32).view(g, M)
     xsum = work[a + sb:a + sb + M * g * 4].view(torch.int32).view(g, M)
     return y, (xq, xs, xsum)
+
+
+def _backward_work(M: int, K: int, N: int, work, device):
+    nbytes = int(lib().q4_backward_work_bytes(M, K, N))
+    if nbytes == 0:
+        raise ValueError("invalid shape for the input gradient (K must be a multiple of 256)")
+    if work is None:
+        return torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    if work.numel() * work.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return work
+
+
+def q4k_gemm_backward(blocks, dy, K: int, dx=None, work=None, stream=None):
+    """Input gradient with frozen Q4_K weights: dy [M][N] -> dx [M][K] = dy . dequant(W)."""
+    M, N = dy.shape
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    work = _backward_work(M, K, N, work, dy.device)
+    _check(lib().q4k_gemm_backward(M, K, N, _ptr(blocks), _ptr(dy), _ptr(dx), _ptr(work), _stream(stream)),
+           "q4k_gemm_backward")
+    return dx
+
+
+def gemm_backward(fmt: str, bs: int, wq, wscale, wbias, dy, dx=None, work=None, bits: int = 4, stream=None):
+    """Input gradient with frozen Q4_0 / affine weights: dy [M][N] -> dx [M][K] = dy . dequant(W)."""
+    M, N = dy.shape
+    K = 2 * wq.shape[1]
+    if dx is None:
+        dx = torch.empty((M, K), dtype=torch.float32, device=dy.device)
+    work = _backward_work(M, K, N, work, dy.device)
+    _check(lib().q4_gemm_backward(M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(wscale), _ptr(wbias), _ptr(dy),
+                                  _ptr(dx), _ptr(work), _stream(stream)), "q4_gemm_backward")
+    return dx
 
 
 def q4k_gemv(blocks, x, N: int, y=None, stream=None):

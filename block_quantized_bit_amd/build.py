@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libq4.so")
-SOURCES = ["api.hip", "act_quant.hip", "gemv.hip", "gemm.hip", "gemm_small.hip", "q4k.hip", "wquant.hip"]
+SOURCES = ["api.hip", "act_quant.hip", "gemv.hip", "gemm.hip", "gemm_small.hip", "backward.hip", "q4k.hip", "wquant.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

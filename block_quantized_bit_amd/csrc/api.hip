@@ -199,6 +199,45 @@ int q4_gemm_packed(int M, int K, int N, int bs, int fmt, int bits, int xdtype, c
     return hip_status(q4::launch_gemm_packed(M, K, N, bs, fmt, packed, xq, xs, xsum, y, s));
 }
 
+// Shapes of the input-gradient entry points: K a multiple of 256, 32-bit buffer offsets.
+static int backward_shape(int M, int K, int N, int fmt) {
+    if (M <= 0 || N <= 0 || K <= 0) return Q4_ERR_DIM;
+    if (K % 256 != 0) return Q4_ERR_BLOCK;
+    const long long wbytes = fmt == 2 ? (long long)N * (K / 256) * 144 : (long long)N * (K / 2);
+    if (wbytes >= (1LL << 31) || (long long)M * N * 4 >= (1LL << 31)) return Q4_ERR_DIM;
+    return Q4_OK;
+}
+
+size_t q4_backward_work_bytes(int M, int K, int N) {
+    if (backward_shape(M, K, N, 2) || backward_shape(M, K, N, 0)) return 0;
+    return (size_t)q4::backward_ranges(M, K, N) * M * K * sizeof(float);
+}
+
+int q4k_gemm_backward(int M, int K, int N, const void* blocks, const float* dy, float* dx, void* work, void* stream) {
+    int st = backward_shape(M, K, N, 2);
+    if (st) return st;
+    if (!blocks || !dy || !dx || !work) return Q4_ERR_NULL;
+    if (!aligned(blocks, 16) || !aligned(dy, 4) || !aligned(dx, 4) || !aligned(work, 4)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_backward(M, K, N, 2, 256, static_cast<const uint8_t*>(blocks), nullptr, nullptr, dy,
+                                          dx, static_cast<float*>(work), static_cast<hipStream_t>(stream)));
+}
+
+int q4_gemm_backward(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
+                     const void* wbias, const float* dy, float* dx, void* work, void* stream) {
+    if (bits != 4) return Q4_ERR_FORMAT;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE) return Q4_ERR_FORMAT;
+    int st = block_status(K > 0 ? K : bs, bs, fmt);
+    if (st) return st;
+    st = backward_shape(M, K, N, fmt);
+    if (st) return st;
+    if (!wq || !wscale || !dy || !dx || !work || (fmt == Q4_FMT_AFFINE && !wbias)) return Q4_ERR_NULL;
+    if (!aligned(wq, 16) || !aligned(wscale, 2) || (wbias && !aligned(wbias, 2)) || !aligned(dy, 4) ||
+        !aligned(dx, 4) || !aligned(work, 4))
+        return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_backward(M, K, N, fmt, bs, wq, wscale, wbias, dy, dx, static_cast<float*>(work),
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int q4k_gemv(int M, int K, int N, const void* blocks, const float* x, float* y, void* stream) {
     if (!blocks || !x || !y) return Q4_ERR_NULL;
     if (M != 1 || N <= 0 || K <= 0) return Q4_ERR_DIM;

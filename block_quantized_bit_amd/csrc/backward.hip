@@ -1,0 +1,225 @@
+// Input gradient with frozen 4-bit weights: dX [M][K] = dY [M][N] . dequant(W [N][K]).
+//
+// C-Kernel-Engine gemm_kernels_q4k.c, section "Backward Pass: Gradient w.r.t.
+// Input": dL/dX = W^T . dL/dY with the weights dequantized on the fly and no
+// weight gradient (the weights are frozen); the batched form is one such
+// product per activation row. The same product is provided for Q4_0 and
+// affine weights.
+//
+// The contraction runs over N, the weight rows. A workgroup owns one 256-wide
+// column of K (one Q4_K super-block, or 8 Q4_0 blocks / 4 or 2 affine groups),
+// one 16-row tile of dY and one range of weight rows. Every weight byte of the
+// column and range is read once. Rows are staged through LDS 64 at a time in a
+// common form: the column's 128 code bytes of the row and eight (a, b) pairs,
+// one per 32-weight sub-block, with w = a*q + b:
+//   Q4_K:   a = d * sc[s], b = -dmin * m[s]      (gemv_q4_k_ref: "w = d * q - m")
+//   Q4_0:   a = d,         b = -8 d
+//   affine: a = scale,     b = bias              of the sub-block's group
+// Each of the 4 wavefronts owns 64 of the 256 k (four 16-wide tiles) and runs
+// v_mfma_f32_16x16x4_f32 with dY rows as A (16 m x 4 n) and the dequantized
+// weights as B (4 n x 16 k): each lane dequantizes one weight per MFMA.
+// A second pass adds the per-range partial sums in a fixed order (no atomics).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace q4 {
+
+namespace {
+
+constexpr int BT = 256;       // threads per workgroup (4 wavefronts)
+constexpr int KCOL = 256;     // K per workgroup
+constexpr int RC = 64;        // weight rows per LDS stage
+constexpr int Q4K_BYTES = 144;
+constexpr int RSRC_WORD3 = 0x00020000;
+constexpr uint32_t OUT = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
+}
+
+struct BwdLds {
+    uint8_t codes[RC][128 + 16];  // 16 bytes of padding per row
+    float2 coef[RC][8];           // (a, b) per 32-weight sub-block
+    float dy[16][RC + 4];         // dY tile, [m][n]
+};
+
+// Byte index and nibble shift of weight k (0..255) of a column.
+template <int FMTB>
+__device__ __forceinline__ void code_pos(int k, int& byte, int& shift) {
+    if (FMTB == 2) {  // Q4_K: chunk c of 64 weights: low nibbles of qs[32c ..], then their high nibbles
+        const int c = k >> 6, r = k & 63;
+        byte = 32 * c + (r & 31);
+        shift = (r >> 5) * 4;
+    } else {          // Q4_0 / affine: block b of 32: low nibbles of bytes 16b .., then high nibbles
+        const int b = k >> 5, j = k & 31;
+        byte = 16 * b + (j & 15);
+        shift = (j >> 4) * 4;
+    }
+}
+
+// FMTB: 0 Q4_0 (G = 32), 1 affine (G = 64 / 128), 2 Q4_K (G = 256).
+template <int FMTB, int G>
+__global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, int N, int rows_per, const uint8_t* __restrict__ w,
+                                                                 const uint16_t* __restrict__ wscale,
+                                                                 const uint16_t* __restrict__ wbias,
+                                                                 const float* __restrict__ dy, float* __restrict__ work) {
+    __shared__ BwdLds S;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kb = blockIdx.x, nc = blockIdx.y, m0 = blockIdx.z * 16;
+    const int nbeg = nc * rows_per, nend = min(N, nbeg + rows_per);
+    const int ngroups = K / G;
+
+    const uint32_t wbytes = FMTB == 2 ? (uint32_t)((size_t)N * (K / 256) * Q4K_BYTES) : (uint32_t)((size_t)N * (K / 2));
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(w, wbytes);
+    const __amdgpu_buffer_rsrc_t r_s = rsrc(wscale, FMTB == 2 ? 0u : (uint32_t)((size_t)N * ngroups * 2));
+    const __amdgpu_buffer_rsrc_t r_b = rsrc(wbias, FMTB == 1 ? (uint32_t)((size_t)N * ngroups * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t r_dy = rsrc(dy, (uint32_t)((size_t)M * N * 4));
+
+    // this lane's four weights per MFMA step: column k = 64*wave + 16*j + lane%16
+    int bidx[4], bsh[4], bsub[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int k = 64 * wave + 16 * j + (lane & 15);
+        code_pos<FMTB>(k, bidx[j], bsh[j]);
+        bsub[j] = k >> 5;
+    }
+    v4f acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int r0 = nbeg; r0 < nend; r0 += RC) {
+        // codes: 4 threads x 32 bytes per row
+        {
+            const int r = tid >> 2, part = tid & 3, n = r0 + r;
+            uint32_t o = OUT;
+            if (n < nend) {
+                o = FMTB == 2 ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES + 16 + 32 * part)
+                              : (uint32_t)((size_t)n * (K / 2) + (size_t)kb * 128 + 32 * part);
+            }
+            // Q4_K blocks are 144 bytes: 16-byte aligned offsets (144 = 9 * 16), so 128-bit loads
+            const uint4 v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
+            const uint4 v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 16, 0, 0));
+            *reinterpret_cast<uint4*>(&S.codes[r][32 * part]) = v0;
+            *reinterpret_cast<uint4*>(&S.codes[r][32 * part + 16]) = v1;
+        }
+        // coefficients: 4 threads x 2 sub-blocks per row
+        {
+            const int r = tid >> 2, s0 = 2 * (tid & 3), n = r0 + r;
+            const bool in = n < nend;
+            float2 c0 = make_float2(0.0f, 0.0f), c1 = make_float2(0.0f, 0.0f);
+            if (FMTB == 2) {
+                const uint32_t o = in ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES) : OUT;
+                const uint4 h = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
+                const float d = half_to_float(h.x & 0xFFFFu), dmin = half_to_float(h.x >> 16);
+                // the sixteen 6-bit fields of the 96-bit little-endian string in h.y, h.z, h.w
+                const uint64_t lo = ((uint64_t)h.z << 32) | h.y;
+                const uint32_t hi = h.w;
+                auto field = [&](int f) -> uint32_t {
+                    const int bit = 6 * f;
+                    if (bit + 6 <= 64) return (uint32_t)(lo >> bit) & 63u;
+                    if (bit >= 64) return (hi >> (bit - 64)) & 63u;
+                    return (uint32_t)((lo >> bit) | ((uint64_t)hi << (64 - bit))) & 63u;
+                };
+                c0 = make_float2(d * (float)field(s0), -dmin * (float)field(8 + s0));
+                c1 = make_float2(d * (float)field(s0 + 1), -dmin * (float)field(8 + s0 + 1));
+            } else {
+                const int g0 = (kb * 256 + 32 * s0) / G, g1 = (kb * 256 + 32 * (s0 + 1)) / G;
+                const uint32_t ob = in ? (uint32_t)((size_t)n * ngroups * 2) : OUT;
+                const float a0 = (FMTB == 0) ? half_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g0 * 2, 0))
+                                             : bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g0 * 2, 0));
+                const float a1 = (FMTB == 0) ? half_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g1 * 2, 0))
+                                             : bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g1 * 2, 0));
+                if (FMTB == 0) {
+                    c0 = make_float2(a0, -8.0f * a0);
+                    c1 = make_float2(a1, -8.0f * a1);
+                } else {
+                    c0 = make_float2(a0, bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g0 * 2, 0)));
+                    c1 = make_float2(a1, bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g1 * 2, 0)));
+                }
+            }
+            S.coef[r][s0] = c0;
+            S.coef[r][s0 + 1] = c1;
+        }
+        // dY tile: 16 rows x 64 weight rows, 4 values per thread
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + BT * i, m = idx >> 6, r = idx & 63, n = r0 + r;
+            const uint32_t o = (m0 + m < M && n < nend) ? (uint32_t)(((size_t)(m0 + m) * N + n) * 4) : OUT;
+            S.dy[m][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_dy, o, 0, 0));
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int st = 0; st < RC / 4; ++st) {
+            const int rl = 4 * st + (lane >> 4);  // this lane's weight row in the stage
+            const float aop = S.dy[lane & 15][rl];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = (S.codes[rl][bidx[j]] >> bsh[j]) & 15;
+                const float2 c = S.coef[rl][bsub[j]];
+                const float wv = c.x * (float)q + c.y;
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, wv, acc[j], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    // D layout: lane holds column lane%16, rows 4*(lane/16) + r
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int k = kb * KCOL + 64 * wave + 16 * j + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * (lane >> 4) + r;
+            if (m < M) work[((size_t)nc * M + m) * K + k] = acc[j][r];
+        }
+    }
+}
+
+// dx[m][k] = sum over ranges c of work[c][m][k], in range order.
+__global__ __launch_bounds__(256) void backward_reduce_kernel(long long total, int nranges, const float* __restrict__ work,
+                                                              float* __restrict__ dx) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    float s = 0.0f;
+    for (int c = 0; c < nranges; ++c) s += work[(size_t)c * total + i];
+    dx[i] = s;
+}
+
+template <int FMTB, int G>
+hipError_t launch_b(int M, int K, int N, const uint8_t* w, const void* ws, const void* wb, const float* dy, float* dx,
+                    float* work, hipStream_t stream) {
+    const int nr = backward_ranges(M, K, N);
+    const int rows_per = (N + nr - 1) / nr;
+    const dim3 grid(K / KCOL, nr, (M + 15) / 16);
+    hipLaunchKernelGGL((backward_partial_kernel<FMTB, G>), grid, dim3(BT), 0, stream, M, K, N, rows_per, w,
+                       static_cast<const uint16_t*>(ws), static_cast<const uint16_t*>(wb), dy, work);
+    const long long total = (long long)M * K;
+    hipLaunchKernelGGL(backward_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, nr,
+                       work, dx);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Weight-row ranges: enough workgroups to fill the chip (about 512), ranges
+// of at least 64 rows.
+int backward_ranges(int M, int K, int N) {
+    const long long cols = (long long)(K / KCOL) * ((M + 15) / 16);
+    long long nr = (512 + cols - 1) / cols;
+    const long long max_nr = (N + RC - 1) / RC;
+    if (nr > max_nr) nr = max_nr;
+    if (nr < 1) nr = 1;
+    return (int)nr;
+}
+
+hipError_t launch_backward(int M, int K, int N, int fmt, int bs, const uint8_t* w, const void* wscale,
+                           const void* wbias, const float* dy, float* dx, float* work, hipStream_t stream) {
+    if (fmt == 2) return launch_b<2, 256>(M, K, N, w, nullptr, nullptr, dy, dx, work, stream);
+    if (fmt == 0) return launch_b<0, 32>(M, K, N, w, wscale, nullptr, dy, dx, work, stream);
+    if (bs == 64) return launch_b<1, 64>(M, K, N, w, wscale, wbias, dy, dx, work, stream);
+    if (bs == 128) return launch_b<1, 128>(M, K, N, w, wscale, wbias, dy, dx, work, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace q4

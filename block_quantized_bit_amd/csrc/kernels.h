@@ -46,6 +46,12 @@ hipError_t launch_pack_weights(int N, int K, int bs, int fmt, const uint8_t* wq,
 hipError_t launch_gemm_packed(int M, int K, int N, int bs, int fmt, const uint8_t* packed, const int8_t* xq,
                               const float* xs_gm, const int32_t* xsum_gm, float* y, hipStream_t stream);
 
+// Input gradient with frozen weights, dx = dy . dequant(W); fmt 0 Q4_0, 1 affine
+// (bs 64 / 128), 2 Q4_K. K % 256 == 0. work: backward_ranges(M, K, N) * M * K floats.
+int backward_ranges(int M, int K, int N);
+hipError_t launch_backward(int M, int K, int N, int fmt, int bs, const uint8_t* w, const void* wscale,
+                           const void* wbias, const float* dy, float* dx, float* work, hipStream_t stream);
+
 hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
 hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
 

@@ -229,6 +229,26 @@ size_t q4_gemm_packed_work_bytes(int M, int K, int bs);
 int q4_gemm_packed(int M, int K, int N, int bs, int fmt, int bits, int xdtype, const void* x,
                    const uint8_t* packed, float* y, void* work, void* stream);
 
+/*
+ * Input gradient with frozen weights (C-Kernel-Engine gemm_kernels_q4k.c,
+ * section "Backward Pass: Gradient w.r.t. Input": dL/dX = W^T . dL/dY with the
+ * weights dequantized on the fly, no weight gradient; the batched form is one
+ * such product per activation row). With W [N][K] as in the forward calls:
+ *   dx[m][k] = sum_n dy[m][n] * w^[n][k],  dy [M][N], dx [M][K] float32,
+ * w^ the dequantized weight (Q4_K: d*sc*q - dmin*m; Q4_0: d*(q - 8);
+ * affine: s*q + b). K must be a multiple of 256 (else Q4_ERR_BLOCK).
+ * work: caller-owned scratch of q4_backward_work_bytes(M, K, N) bytes
+ * (4-byte aligned) for per-row-range partial sums, which a second launch adds
+ * in a fixed order (results do not depend on scheduling).
+ * q4_backward_work_bytes returns 0 for invalid shapes.
+ */
+size_t q4_backward_work_bytes(int M, int K, int N);
+int q4k_gemm_backward(int M, int K, int N, const void* blocks, const float* dy, float* dx,
+                      void* work, void* stream);
+int q4_gemm_backward(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq,
+                     const void* wscale, const void* wbias, const float* dy, float* dx,
+                     void* work, void* stream);
+
 /* Static name of a q4_status value ("unknown status" otherwise). */
 const char* q4_status_string(int status);
 

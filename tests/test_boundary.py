@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None
@@ -147,6 +147,26 @@ def test_packed_sizes_and_validation():
     assert g(*args) == ALIGN
     args = list(base); args[0] = 0
     assert g(*args) == DIM
+
+
+def test_backward_validation():
+    L = q4.lib()
+    assert L.q4_backward_work_bytes(1, 4096, 14336) > 0
+    assert L.q4_backward_work_bytes(1, 4000, 14336) == 0
+    assert L.q4_backward_work_bytes(0, 4096, 8) == 0
+    f = L.q4k_gemm_backward
+    assert f(1, 512, 8, None, A, A, A, None) == NULL
+    assert f(1, 500, 8, A, A, A, A, None) == BLOCK
+    assert f(1, 512, 0, A, A, A, A, None) == DIM
+    assert f(1, 512, 8, A + 8, A, A, A, None) == ALIGN
+    assert f(1, 512, 8, A, A, A, None, None) == NULL
+    g = L.q4_gemm_backward
+    assert g(1, 512, 8, 32, 0, 8, A, A, None, A, A, A, None) == FORMAT
+    assert g(1, 512, 8, 32, 3, 4, A, A, None, A, A, A, None) == FORMAT
+    assert g(1, 512, 8, 64, 0, 4, A, A, None, A, A, A, None) == BLOCK
+    assert g(1, 96, 8, 32, 0, 4, A, A, None, A, A, A, None) == BLOCK          # K not a multiple of 256
+    assert g(1, 512, 8, 64, 1, 4, A, A, None, A, A, A, None) == NULL          # affine needs biases
+    assert g(1, 512, 8, 32, 0, 4, A, A + 1, None, A, A, A, None) == ALIGN
 
 
 def test_q4k_validation():

@@ -458,6 +458,69 @@ def test_gemm_packed_workload_sampled(name):
     assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
 
 
+# ---------------------------------------------------------------- input gradient, frozen weights
+
+BWD_SHAPES = [(1, 256, 1), (3, 512, 70), (16, 1024, 129), (17, 768, 200), (33, 256, 64)]
+
+
+@pytest.mark.parametrize("M,K,N", BWD_SHAPES)
+def test_q4k_backward_ragged(M, K, N):
+    print(f"case q4k backward M={M} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(M * 31 + K + N)
+    blocks = oracle.quantize_q4k((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    dy = rng.standard_normal((M, N)).astype(np.float32)
+    dx = q4.q4k_gemm_backward(to_dev(blocks), to_dev(dy), K)
+    _sync()
+    assert rel_rms(to_np(dx), oracle.q4k_backward(blocks, dy, K, N)) <= TOL
+
+
+@pytest.mark.parametrize("fmt,bs", [("q4_0", 32), ("affine", 64), ("affine", 128)])
+@pytest.mark.parametrize("M,K,N", BWD_SHAPES)
+def test_q4_backward_ragged(fmt, bs, M, K, N):
+    print(f"case backward {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
+    wts, _ = _partials_case(fmt, bs, 1, K, N, 19 * M + K + N)
+    dy = np.random.default_rng(K + 3 * N).standard_normal((M, N)).astype(np.float32)
+    dx = q4.gemm_backward(fmt, bs, *_wts_dev(fmt, wts), to_dev(dy))
+    _sync()
+    wb = wts[2] if fmt == "affine" else None
+    ref = oracle.q4_backward(wts[0], wts[1], wb, dy, K, N, bs, FMT[fmt])
+    assert rel_rms(to_np(dx), ref) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_q4k_backward_workload(M):
+    # the Q4_K workload's weights (N=14336, K=4096); dY drawn N(0,1)
+    print(f"case q4k backward workload M={M}", flush=True)
+    wl, _, _, _, blocks = workload_data("q4_k_gemv_1x4096x14336")
+    dy = np.random.default_rng(4242 + M).standard_normal((M, wl.N)).astype(np.float32)
+    gb, gdy = to_dev(blocks), to_dev(dy)
+    dx = q4.q4k_gemm_backward(gb, gdy, wl.K)
+    dx2 = q4.q4k_gemm_backward(gb, gdy, wl.K)
+    _sync()
+    assert torch.equal(dx, dx2)
+    ms, ks = sample_pairs(M, wl.K, 400, 77 + M)
+    ref = oracle.q4k_backward_sample(blocks, dy, wl.K, wl.N, ms, ks)
+    assert rel_rms(to_np(dx)[ms, ks], ref) <= TOL
+    # adjoint of the GPU forward product at full size: <dY, W x> = <dX, x>
+    x = np.random.default_rng(5 + M).standard_normal((M, wl.K)).astype(np.float32)
+    y = q4.q4k_gemm(gb, to_dev(x), wl.N) if M > 1 else q4.q4k_gemv(gb, to_dev(x), wl.N)
+    _sync()
+    lhs = float((dy.astype(np.float64) * to_np(y).astype(np.float64)).sum())
+    rhs = float((to_np(dx).astype(np.float64) * x.astype(np.float64)).sum())
+    assert abs(lhs - rhs) <= 1e-4 * np.sqrt(M * wl.N) * np.abs(to_np(y)).mean()
+
+
+def test_q4_backward_decode_workload_sampled():
+    print("case backward q4_0 decode weights M=4", flush=True)
+    wl, _, _, _, wts = workload_data("q4_0_decode_4096")
+    dy = np.random.default_rng(808).standard_normal((4, wl.N)).astype(np.float32)
+    dx = q4.gemm_backward("q4_0", 32, *_wts_dev("q4_0", wts), to_dev(dy))
+    _sync()
+    ms, ks = sample_pairs(4, wl.K, 400, 9)
+    ref = oracle.q4_backward_sample(wts[0], wts[1], None, dy, wl.K, wl.N, 32, FMT["q4_0"], ms, ks)
+    assert rel_rms(to_np(dx)[ms, ks], ref) <= TOL
+
+
 # ---------------------------------------------------------------- Q4_K
 
 def test_q4k_gemv_workload():
