@@ -72,6 +72,13 @@ def lib() -> ctypes.CDLL:
         L.or_q4k_gemm.argtypes = [I, I, I, P, P, P]
         L.or_q4k_gemm_sample.argtypes = [I, I, I, P, P, I, P, P, P]
         L.or_q4k_backward.argtypes = [I, I, I, P, P, P]
+        L.or_code_bytes.argtypes = [I, I, I]
+        L.or_code_bytes.restype = ctypes.c_long
+        L.or_get_code_bits.argtypes = [P, I, I, I, I, I]
+        L.or_quantize_affine_bits.argtypes = [I, I, I, I, P, P, P, P]
+        L.or_q4_partials_bits.argtypes = [I, I, I, I, I, I, P, P, I, I, P]
+        L.or_q4_gemm_bits.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+        L.or_q4_gemm_sample_bits.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, I, P, P, P]
         L.or_q4_backward.argtypes = [I, I, I, I, I, P, P, P, P, P]
         L.or_q4k_backward_sample.argtypes = [I, I, I, P, P, I, P, P, P]
         L.or_q4_backward_sample.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, P]
@@ -144,14 +151,20 @@ def quantize_q4_0(w: np.ndarray):
     return wq, wd
 
 
-def quantize_affine(w_bf16: np.ndarray, g: int):
-    """w [N][K] bfloat16 bits -> (wq uint8 [N][K/2], ws, wb bfloat16 bits [N][K/g])."""
+def code_array_shape(N: int, K: int, bits: int):
+    """Shape of the code array at a bit width: [N][K/2] (4), [N][K] (8), or one flat buffer of
+    N*K*3/4 bytes (6: the low-nibble layout of 4 bits, then the high 2-bit plane)."""
+    return {4: (N, K // 2), 8: (N, K), 6: (N * K * 3 // 4,)}[bits]
+
+
+def quantize_affine(w_bf16: np.ndarray, g: int, bits: int = 4):
+    """w [N][K] bfloat16 bits -> (wq uint8 codes, ws, wb bfloat16 bits [N][K/g]); codes 0 .. 2^bits - 1."""
     w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
     N, K = w.shape
-    wq = np.empty((N, K // 2), dtype=np.uint8)
+    wq = np.empty(code_array_shape(N, K, bits), dtype=np.uint8)
     ws = np.empty((N, K // g), dtype=np.uint16)
     wb = np.empty((N, K // g), dtype=np.uint16)
-    _ok(lib().or_quantize_affine(N, K, g, _p(w), _p(wq), _p(ws), _p(wb)), "quantize_affine")
+    _ok(lib().or_quantize_affine_bits(N, K, g, bits, _p(w), _p(wq), _p(ws), _p(wb)), "quantize_affine")
     return wq, ws, wb
 
 
@@ -164,9 +177,13 @@ def quantize_q4k(w: np.ndarray) -> np.ndarray:
     return blocks
 
 
-def get_code(wq: np.ndarray, K: int, n: int, k: int) -> int:
+def get_code(wq: np.ndarray, K: int, n: int, k: int, bits: int = 4, N: int | None = None) -> int:
     wq = np.ascontiguousarray(wq, dtype=np.uint8)
-    return lib().or_get_code(_p(wq), K, n, k)
+    if bits == 4:
+        return lib().or_get_code(_p(wq), K, n, k)
+    if N is None:
+        N = wq.size * 8 // (K * bits)
+    return lib().or_get_code_bits(_p(wq), N, K, bits, n, k)
 
 
 def q4k_pack_scales(sc, mn) -> np.ndarray:
@@ -194,13 +211,13 @@ def q4k_dequant(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
 
 # ---- results ---------------------------------------------------------------
 
-def q4_partials(wq, xq, K: int, N: int, bs: int, fmt: int, m0: int = 0, m1: int | None = None):
+def q4_partials(wq, xq, K: int, N: int, bs: int, fmt: int, m0: int = 0, m1: int | None = None, bits: int = 4):
     wq = np.ascontiguousarray(wq, dtype=np.uint8)
     xq = np.ascontiguousarray(xq, dtype=np.int8)
     M = xq.shape[0]
     m1 = M if m1 is None else m1
     out = np.empty((m1 - m0, N, K // bs), dtype=np.int32)
-    _ok(lib().or_q4_partials(M, K, N, bs, fmt, _p(wq), _p(xq), m0, m1, _p(out)), "q4_partials")
+    _ok(lib().or_q4_partials_bits(M, K, N, bs, fmt, bits, _p(wq), _p(xq), m0, m1, _p(out)), "q4_partials")
     return out
 
 
@@ -210,7 +227,7 @@ def _scales(wscale, wbias):
     return ws, wb
 
 
-def q4_gemm(wq, wscale, wbias, xq, xs, xsum, K: int, N: int, bs: int, fmt: int) -> np.ndarray:
+def q4_gemm(wq, wscale, wbias, xq, xs, xsum, K: int, N: int, bs: int, fmt: int, bits: int = 4) -> np.ndarray:
     wq = np.ascontiguousarray(wq, dtype=np.uint8)
     ws, wb = _scales(wscale, wbias)
     xq = np.ascontiguousarray(xq, dtype=np.int8)
@@ -218,13 +235,13 @@ def q4_gemm(wq, wscale, wbias, xq, xs, xsum, K: int, N: int, bs: int, fmt: int) 
     xsum = np.ascontiguousarray(xsum, dtype=np.int32)
     M = xq.shape[0]
     y = np.empty((M, N), dtype=np.float32)
-    _ok(lib().or_q4_gemm(M, K, N, bs, fmt, _p(wq), _p(ws), None if wb is None else _p(wb),
-                         _p(xq), _p(xs), _p(xsum), _p(y)), "q4_gemm")
+    _ok(lib().or_q4_gemm_bits(M, K, N, bs, fmt, bits, _p(wq), _p(ws), None if wb is None else _p(wb),
+                              _p(xq), _p(xs), _p(xsum), _p(y)), "q4_gemm")
     return y
 
 
 def q4_gemm_sample(wq, wscale, wbias, xq, xs, xsum, K: int, N: int, bs: int, fmt: int,
-                   ms, ns) -> np.ndarray:
+                   ms, ns, bits: int = 4) -> np.ndarray:
     wq = np.ascontiguousarray(wq, dtype=np.uint8)
     ws, wb = _scales(wscale, wbias)
     xq = np.ascontiguousarray(xq, dtype=np.int8)
@@ -234,8 +251,8 @@ def q4_gemm_sample(wq, wscale, wbias, xq, xs, xsum, K: int, N: int, bs: int, fmt
     ns = np.ascontiguousarray(ns, dtype=np.int32)
     M = xq.shape[0]
     y = np.empty(ms.shape[0], dtype=np.float32)
-    _ok(lib().or_q4_gemm_sample(M, K, N, bs, fmt, _p(wq), _p(ws), None if wb is None else _p(wb),
-                                _p(xq), _p(xs), _p(xsum), ms.shape[0], _p(ms), _p(ns), _p(y)),
+    _ok(lib().or_q4_gemm_sample_bits(M, K, N, bs, fmt, bits, _p(wq), _p(ws), None if wb is None else _p(wb),
+                                     _p(xq), _p(xs), _p(xsum), ms.shape[0], _p(ms), _p(ns), _p(y)),
         "q4_gemm_sample")
     return y
 

@@ -41,6 +41,12 @@
  *     xs * sum(xq) of the group, so y equals dequant(W) . dequant(X) exactly;
  *   - code layout: block b of row n is 16 bytes at offset 16 b; byte j holds
  *     k = 32 b + j in its low nibble and k = 32 b + 16 + j in its high nibble;
+ *   - affine 8-bit ([mlx] lists 4, 6 and 8 bits): wq [N][K], byte k = code k;
+ *     affine 6-bit: the low 4 bits of every code in the 4-bit layout above
+ *     (N x K/2 bytes), then the high 2 bits as N x K/4 bytes: block b of row n
+ *     is 8 bytes at offset 8 b, two little-endian words; word h holds code
+ *     32 b + 16 h + c (c = 0..15) in byte c % 4, bits 2 (c / 4) and 2 (c / 4) + 1;
+ *     scale = bf16((max - min) / (2^bits - 1)), codes 0 .. 2^bits - 1;
  *   - Q4_K struct {fp16 d; fp16 dmin; u8 scales[12]; u8 qs[128]} with the
  *     sixteen 6-bit fields (sc[0..7], m[0..7]) packed little-endian, field f at
  *     bits [6f, 6f + 6) of the 96-bit string.
@@ -193,6 +199,39 @@ int or_get_code(const uint8_t* wq, int K, int n, int k) {
     return get_code(wq + (long)n * (K / 2), k);
 }
 
+/* Code of weight (n, k) at a bit width (4, 6 or 8), per the layouts above. */
+static int code_at(const uint8_t* wq, int N, int K, int bits, long n, int k) {
+    if (bits == 8) return wq[n * (long)K + k];
+    int lo = get_code(wq + n * (long)(K / 2), k);
+    if (bits == 4) return lo;
+    const uint8_t* hp = wq + (long)N * (K / 2) + n * (long)(K / 4);
+    int b = k / 32, j = k % 32, h = j / 16, c = j % 16;
+    int hi2 = (hp[8 * b + 4 * h + (c % 4)] >> (2 * (c / 4))) & 3;
+    return lo | (hi2 << 4);
+}
+
+static void put_code_at(uint8_t* wq, int N, int K, int bits, long n, int k, int q) {
+    if (bits == 8) { wq[n * (long)K + k] = (uint8_t)q; return; }
+    put_code(wq + n * (long)(K / 2), k, q & 0x0F);
+    if (bits == 4) return;
+    uint8_t* hp = wq + (long)N * (K / 2) + n * (long)(K / 4);
+    int b = k / 32, j = k % 32, h = j / 16, c = j % 16;
+    uint8_t* byte = hp + 8 * b + 4 * h + (c % 4);
+    int sh = 2 * (c / 4);
+    *byte = (uint8_t)((*byte & ~(3 << sh)) | (((q >> 4) & 3) << sh));
+}
+
+static int bits_ok(int bits) { return bits == 4 || bits == 6 || bits == 8; }
+
+long or_code_bytes(int N, int K, int bits) {
+    if (!bits_ok(bits) || N < 0 || K <= 0 || K % 32 != 0) return -1;
+    return (long)N * K * bits / 8;
+}
+
+int or_get_code_bits(const uint8_t* wq, int N, int K, int bits, int n, int k) {
+    return code_at(wq, N, K, bits, n, k);
+}
+
 /* Q4_0 ([tract]: 4-bit codes, N x K, one fp16 scale per 32-block):
  * w [N][K] float32 -> wq [N][K/2], wd [N][K/32] fp16 bits. */
 int or_quantize_q4_0(int N, int K, const float* w, uint8_t* wq, uint16_t* wd) {
@@ -224,15 +263,16 @@ int or_quantize_q4_0(int N, int K, const float* w, uint8_t* wq, uint16_t* wd) {
     return OR_OK;
 }
 
-/* Affine 4-bit ([mlx]: per-group scale and bias, codes 0..15):
- * w [N][K] bfloat16 bits -> wq [N][K/2], ws, wb [N][K/g] bfloat16 bits. */
-int or_quantize_affine(int N, int K, int g, const uint16_t* w, uint8_t* wq,
-                       uint16_t* ws, uint16_t* wb) {
-    if (N < 0 || K <= 0 || g <= 0 || g % 32 != 0 || K % g != 0) return OR_BAD;
+/* Affine ([mlx]: per-group scale and bias, codes 0 .. 2^bits - 1, bits 4, 6
+ * or 8): w [N][K] bfloat16 bits -> wq (or_code_bytes(N, K, bits) bytes),
+ * ws, wb [N][K/g] bfloat16 bits. */
+int or_quantize_affine_bits(int N, int K, int g, int bits, const uint16_t* w, uint8_t* wq,
+                            uint16_t* ws, uint16_t* wb) {
+    if (N < 0 || K <= 0 || g <= 0 || g % 32 != 0 || K % g != 0 || !bits_ok(bits)) return OR_BAD;
     int ng = K / g;
+    int qmax = (1 << bits) - 1;
+    memset(wq, 0, (size_t)or_code_bytes(N, K, bits));
     for (long n = 0; n < N; ++n) {
-        uint8_t* row = wq + n * (K / 2);
-        memset(row, 0, (size_t)K / 2);
         for (int gi = 0; gi < ng; ++gi) {
             const uint16_t* grp = w + n * (long)K + (long)g * gi;
             float mn = or_bf16_to_f32(grp[0]), mx = mn;
@@ -242,7 +282,7 @@ int or_quantize_affine(int N, int K, int g, const uint16_t* w, uint8_t* wq,
                 if (v > mx) mx = v;
             }
             float range = mx - mn;
-            uint16_t s16 = or_f32_to_bf16(range / 15.0f);
+            uint16_t s16 = or_f32_to_bf16(range / (float)qmax);
             uint16_t b16 = or_f32_to_bf16(mn);
             float sf = or_bf16_to_f32(s16), bf = or_bf16_to_f32(b16);
             ws[n * ng + gi] = s16;
@@ -253,13 +293,17 @@ int or_quantize_affine(int N, int K, int g, const uint16_t* w, uint8_t* wq,
                     float t = or_bf16_to_f32(grp[j]) - bf;
                     q = (int)nearbyintf(t / sf);
                     if (q < 0) q = 0;
-                    if (q > 15) q = 15;
+                    if (q > qmax) q = qmax;
                 }
-                put_code(row, g * gi + j, q);
+                put_code_at(wq, N, K, bits, n, g * gi + j, q);
             }
         }
     }
     return OR_OK;
+}
+
+int or_quantize_affine(int N, int K, int g, const uint16_t* w, uint8_t* wq, uint16_t* ws, uint16_t* wb) {
+    return or_quantize_affine_bits(N, K, g, 4, w, wq, ws, wb);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -269,18 +313,26 @@ int or_quantize_affine(int N, int K, int g, const uint16_t* w, uint8_t* wq,
 /* Per-block integer dot of row n of the weights with row m of the codes.
  * fmt 0 (Q4_0): sum (q - 8) * xq over the block of bs = 32.
  * fmt 1 (affine): sum q * xq over the group of bs. */
-static int32_t block_dot(int K, int bs, int fmt, const uint8_t* wq, const int8_t* xq,
+static int32_t block_dot(int N, int K, int bs, int fmt, int bits, const uint8_t* wq, const int8_t* xq,
                          long m, long n, int b) {
-    const uint8_t* row = wq + n * (K / 2);
     const int8_t* xr = xq + m * (long)K;
     int32_t acc = 0;
     for (int j = 0; j < bs; ++j) {
         int k = b * bs + j;
-        int q = get_code(row, k);
+        int q = code_at(wq, N, K, bits, n, k);
         if (fmt == 0) q -= 8;
         acc += (int32_t)q * (int32_t)xr[k];
     }
     return acc;
+}
+
+static int check_fmt_bits(int K, int bs, int fmt, int bits) {
+    if (!bits_ok(bits) || (fmt == 0 && bits != 4)) return OR_BAD;
+    if (K <= 0 || bs <= 0 || K % bs != 0) return OR_BAD;
+    if (fmt == 0 && bs != 32) return OR_BAD;
+    if (fmt == 1 && (bs % 32 != 0)) return OR_BAD;
+    if (fmt != 0 && fmt != 1) return OR_BAD;
+    return OR_OK;
 }
 
 static int check_fmt(int K, int bs, int fmt) {
@@ -291,29 +343,34 @@ static int check_fmt(int K, int bs, int fmt) {
     return OR_OK;
 }
 
-/* partials [(m1 - m0)][N][K/bs] int32 for rows m0 <= m < m1. */
-int or_q4_partials(int M, int K, int N, int bs, int fmt, const uint8_t* wq,
-                   const int8_t* xq, int m0, int m1, int32_t* partials) {
-    if (check_fmt(K, bs, fmt) || m0 < 0 || m1 > M || m0 > m1 || N < 0) return OR_BAD;
+/* partials [(m1 - m0)][N][K/bs] int32 for rows m0 <= m < m1 (bits 4, 6, 8; Q4_0 is 4-bit only). */
+int or_q4_partials_bits(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq,
+                        const int8_t* xq, int m0, int m1, int32_t* partials) {
+    if (check_fmt_bits(K, bs, fmt, bits) || m0 < 0 || m1 > M || m0 > m1 || N < 0) return OR_BAD;
     int nb = K / bs;
     for (long m = m0; m < m1; ++m)
         for (long n = 0; n < N; ++n)
             for (int b = 0; b < nb; ++b)
-                partials[((m - m0) * (long)N + n) * nb + b] = block_dot(K, bs, fmt, wq, xq, m, n, b);
+                partials[((m - m0) * (long)N + n) * nb + b] = block_dot(N, K, bs, fmt, bits, wq, xq, m, n, b);
     return OR_OK;
+}
+
+int or_q4_partials(int M, int K, int N, int bs, int fmt, const uint8_t* wq,
+                   const int8_t* xq, int m0, int m1, int32_t* partials) {
+    return or_q4_partials_bits(M, K, N, bs, fmt, 4, wq, xq, m0, m1, partials);
 }
 
 /* One output y[m][n]:
  *   Q4_0:   sum_b d[n,b] * xs[m,b] * P[m,n,b]
  *   affine: sum_g xs[m,g] * (scale[n,g] * A[m,n,g] + bias[n,g] * xsum[m,g])
  * each term exact in double, summed in block order, rounded once to float. */
-static float one_output(int K, int bs, int fmt, const uint8_t* wq, const uint16_t* wscale,
+static float one_output(int N, int K, int bs, int fmt, int bits, const uint8_t* wq, const uint16_t* wscale,
                         const uint16_t* wbias, const int8_t* xq, const float* xs,
                         const int32_t* xsum, long m, long n) {
     int nb = K / bs;
     double y = 0.0;
     for (int b = 0; b < nb; ++b) {
-        int32_t p = block_dot(K, bs, fmt, wq, xq, m, n, b);
+        int32_t p = block_dot(N, K, bs, fmt, bits, wq, xq, m, n, b);
         double a = (double)xs[m * nb + b];
         if (fmt == 0) {
             double d = (double)or_f16_to_f32(wscale[n * nb + b]);
@@ -328,27 +385,40 @@ static float one_output(int K, int bs, int fmt, const uint8_t* wq, const uint16_
 }
 
 /* y [M][N] float32. */
-int or_q4_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq,
-               const uint16_t* wscale, const uint16_t* wbias, const int8_t* xq,
-               const float* xs, const int32_t* xsum, float* y) {
-    if (check_fmt(K, bs, fmt) || M < 0 || N < 0) return OR_BAD;
+int or_q4_gemm_bits(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq,
+                    const uint16_t* wscale, const uint16_t* wbias, const int8_t* xq,
+                    const float* xs, const int32_t* xsum, float* y) {
+    if (check_fmt_bits(K, bs, fmt, bits) || M < 0 || N < 0) return OR_BAD;
     for (long m = 0; m < M; ++m)
         for (long n = 0; n < N; ++n)
-            y[m * (long)N + n] = one_output(K, bs, fmt, wq, wscale, wbias, xq, xs, xsum, m, n);
+            y[m * (long)N + n] = one_output(N, K, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, m, n);
     return OR_OK;
 }
 
+int or_q4_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq,
+               const uint16_t* wscale, const uint16_t* wbias, const int8_t* xq,
+               const float* xs, const int32_t* xsum, float* y) {
+    return or_q4_gemm_bits(M, K, N, bs, fmt, 4, wq, wscale, wbias, xq, xs, xsum, y);
+}
+
 /* y for the listed (ms[i], ns[i]) only. */
+int or_q4_gemm_sample_bits(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq,
+                           const uint16_t* wscale, const uint16_t* wbias, const int8_t* xq,
+                           const float* xs, const int32_t* xsum, int count, const int* ms,
+                           const int* ns, float* y) {
+    if (check_fmt_bits(K, bs, fmt, bits)) return OR_BAD;
+    for (int i = 0; i < count; ++i) {
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return OR_BAD;
+        y[i] = one_output(N, K, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, ms[i], ns[i]);
+    }
+    return OR_OK;
+}
+
 int or_q4_gemm_sample(int M, int K, int N, int bs, int fmt, const uint8_t* wq,
                       const uint16_t* wscale, const uint16_t* wbias, const int8_t* xq,
                       const float* xs, const int32_t* xsum, int count, const int* ms,
                       const int* ns, float* y) {
-    if (check_fmt(K, bs, fmt)) return OR_BAD;
-    for (int i = 0; i < count; ++i) {
-        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return OR_BAD;
-        y[i] = one_output(K, bs, fmt, wq, wscale, wbias, xq, xs, xsum, ms[i], ns[i]);
-    }
-    return OR_OK;
+    return or_q4_gemm_sample_bits(M, K, N, bs, fmt, 4, wq, wscale, wbias, xq, xs, xsum, count, ms, ns, y);
 }
 
 /* ------------------------------------------------------------------------ */

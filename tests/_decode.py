@@ -60,3 +60,21 @@ def q4k_dequant(blocks: np.ndarray, N: int, K: int) -> np.ndarray:
                 w[64 * c + 32:64 * c + 64] = d * sc[2 * c + 1] * hi - dmin * mn[2 * c + 1]
             out[n, 256 * j:256 * j + 256] = w
     return out
+
+
+def codes_from_bits(wq: np.ndarray, N: int, K: int, bits: int) -> np.ndarray:
+    """Codes [N][K] of a 4-, 6- or 8-bit affine code array.
+    8 bits: one byte per code. 6 bits: the 4-bit layout holds the low 4 bits
+    (N*K/2 bytes), then the high 2 bits follow as N*K/4 bytes: block b of row n
+    is 8 bytes at 8*b, two little-endian words; word h holds code 32b + 16h + c
+    in byte c % 4, bits 2*(c // 4) and 2*(c // 4) + 1."""
+    flat = np.ascontiguousarray(wq).reshape(-1)
+    if bits == 8:
+        return flat.reshape(N, K).astype(np.int64)
+    lo = codes_from_planes(flat[:N * K // 2].reshape(N, K // 2), K)
+    if bits == 4:
+        return lo
+    hp = flat[N * K // 2:].reshape(N, K // 32, 2, 4).astype(np.int64)   # [n][block][word h][byte]
+    c = np.arange(16)
+    hi = (hp[:, :, :, c % 4] >> (2 * (c // 4))) & 3                       # [n][block][h][c]
+    return lo | (hi.reshape(N, K) << 4)
