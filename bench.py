@@ -48,7 +48,7 @@ def parse_args():
     p.add_argument("--only", default=None,
                    help="run one workload alone (for profiling): gemv_fused (eager decode launches, --steps of "
                         "them), gemm_3a, gemm_3b, gemm_2, gemm_0, q4k_gemv, q4k_gemm, act_quant, gemv_plain, "
-                        "small_m, q4k_backward, q4_backward")
+                        "small_m, q4k_backward, q4_backward, gemm_bits")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run a plain device-to-device copy of this many MiB (counter calibration) and exit")
     return p.parse_args()
@@ -322,6 +322,27 @@ def main():
             del packed, work
         secondary[f"prefill_{name}"] = entry
         del gwq, gws, gwb, xq, xs, xsum, yy, xt
+
+    if want("gemm_bits"):
+        # affine 4-, 6- and 8-bit codes on the same int8-MFMA GEMM (two workload shapes, activation codes given)
+        out = {}
+        for name in ("affine_g64_1024x4096x4096", "affine_g128_4096x4096x14336"):
+            g = synth.workload(name)
+            xt = torch.from_numpy(synth.gen.activations(g).view(np.int16)).to(dev).view(torch.bfloat16)
+            wt = torch.from_numpy(synth.gen.weights(g).view(np.int16)).to(dev).view(torch.bfloat16)
+            xq, xs, xsum = q4.quantize_act(xt, g.bs)
+            yy = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
+            ops = 2.0 * g.M * g.N * g.K
+            for bits in (4, 6, 8):
+                gwq, gws, gwb = q4.quantize_weights(wt, "affine", g.bs, bits=bits)
+                t = time_eager(lambda: q4.gemm("affine", g.bs, gwq, gws, gwb, xq, xs, xsum, y=yy, bits=bits),
+                               20 if g.M >= 4096 else 50)
+                out[f"{name}_{bits}bit"] = {"gemm_us": round(t * 1e6, 2), "TOPS": round(ops / t / 1e12, 1),
+                                            "frac_int8_peak": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4),
+                                            "weight_bytes": gwq.numel() + 2 * gws.numel() * 2}
+                del gwq, gws, gwb
+            del xt, wt, xq, xs, xsum, yy
+        secondary["affine_code_widths"] = out
 
     if want("q4k_gemv") or want("q4k_gemm"):
         g1 = synth.workload("q4_k_gemv_1x4096x14336")

@@ -4,7 +4,7 @@ The compute lives in hand-written HIP kernels behind the C ABI in
 include/q4.h; this package only marshals torch device tensors to it.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, LIB_PATH, Q4Error, debug_partials, gemm, gemm_backward, gemm_packed, gemv, gemv_fused, lib, pack_weights,
+    EXPORTS, LIB_PATH, Q4Error, code_shape, debug_partials, gemm, gemm_backward, gemm_packed, gemv, gemv_fused, lib, pack_weights,
     packed_bytes, q4k_gemm, q4k_gemm_backward, q4k_gemv, q4k_quantize_weights, quantize_act, quantize_weights,
     status_string,
 )

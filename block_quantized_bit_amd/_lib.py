@@ -130,11 +130,17 @@ def quantize_act(x: torch.Tensor, bs: int, out=None, stream=None):
     return xq, xs, xsum
 
 
+def code_shape(N: int, K: int, bits: int):
+    """Shape of a code array: [N][K/2] (4 bits), [N][K] (8 bits), or a flat N*K*3/4 bytes (6 bits: the 4-bit
+    nibble layout of the low bits, then the plane of the high 2 bits; layout in include/q4.h)."""
+    return {4: (N, K // 2), 8: (N, K), 6: (N * K * 3 // 4,)}[bits]
+
+
 def _matmul(entry: str, M: int, fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y, bits, stream):
-    N, Kh = wq.shape
-    K = 2 * Kh
-    if xq.shape[1] != K:
-        raise ValueError("xq and wq disagree on K")
+    K = xq.shape[1]
+    N = wscale.shape[0]
+    if wq.numel() * 8 != N * K * bits:
+        raise ValueError("wq does not hold N*K codes of the given width")
     _check(getattr(lib(), entry)(M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(wscale), _ptr(wbias), _ptr(xq),
                                  _ptr(xs), _ptr(xsum), _ptr(y), _stream(stream)), entry)
     return y
@@ -143,7 +149,7 @@ def _matmul(entry: str, M: int, fmt: str, bs: int, wq, wscale, wbias, xq, xs, xs
 def gemv(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int = 4, stream=None):
     """Decode GEMV (xq is [1][K]) -> y float32 [1][N]."""
     if y is None:
-        y = torch.empty((xq.shape[0], wq.shape[0]), dtype=torch.float32, device=wq.device)
+        y = torch.empty((xq.shape[0], wscale.shape[0]), dtype=torch.float32, device=wq.device)
     return _matmul("q4_gemv", xq.shape[0], fmt, bs, wq, wscale, wbias, xq, xs, xsum, y, bits, stream)
 
 
@@ -166,7 +172,7 @@ def gemv_fused(fmt: str, bs: int, x, wq, wscale, wbias, y=None, act_out=None, bi
 def gemm(fmt: str, bs: int, wq, wscale, wbias, xq, xs, xsum, y=None, bits: int = 4, stream=None):
     """Prefill GEMM (xq is [M][K]) -> y float32 [M][N]."""
     if y is None:
-        y = torch.empty((xq.shape[0], wq.shape[0]), dtype=torch.float32, device=wq.device)
+        y = torch.empty((xq.shape[0], wscale.shape[0]), dtype=torch.float32, device=wq.device)
     return _matmul("q4_gemm", xq.shape[0], fmt, bs, wq, wscale, wbias, xq, xs, xsum, y, bits, stream)
 
 
@@ -174,9 +180,8 @@ def debug_partials(path: str, fmt: str, bs: int, wq, xq, xsum, m0: int = 0, m1: 
                    bits: int = 4, stream=None):
     """Exact per-block int32 partials [(m1-m0)][N][K/bs] from the GEMV ('gemv'), tiled GEMM ('gemm') or
     few-row GEMM ('small') kernel."""
-    N, Kh = wq.shape
-    K = 2 * Kh
-    M = xq.shape[0]
+    M, K = xq.shape
+    N = wq.numel() * 8 // (K * bits)
     m1 = M if m1 is None else m1
     if out is None:
         out = torch.empty((max(m1 - m0, 1), N, K // bs), dtype=torch.int32, device=wq.device)
@@ -280,10 +285,12 @@ def q4k_gemm(blocks, x, N: int, y=None, stream=None):
 
 
 def quantize_weights(w: torch.Tensor, fmt: str, bs: int, bits: int = 4, stream=None):
-    """w [N][K] float32 or bfloat16 -> (wq uint8 [N][K/2], wscale, wbias) with fp16 (Q4_0) or bf16 (affine) scales."""
+    """w [N][K] float32 or bfloat16 -> (wq uint8 codes (code_shape), wscale, wbias) with fp16 (Q4_0) or bf16
+    (affine) scales; affine codes may be 4, 6 or 8 bits wide."""
     N, K = w.shape
     f = _fmt(fmt)
-    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    wq = torch.empty(code_shape(N, K, bits) if bits in (4, 6, 8) else (N, K // 2), dtype=torch.uint8,
+                     device=w.device)
     sdt = torch.float16 if f == Q4_FMT_Q4_0 else torch.bfloat16
     ws = torch.empty((N, K // bs), dtype=sdt, device=w.device)
     wb = None if f == Q4_FMT_Q4_0 else torch.empty((N, K // bs), dtype=sdt, device=w.device)

@@ -22,10 +22,20 @@ int block_status(int K, int bs, int fmt) {
     return Q4_OK;
 }
 
+// Code widths: Q4_0 is 4-bit only; affine codes may be 4, 6 or 8 bits wide
+// (MLX PR #4802) where an entry point decodes them. A decoder handed a width
+// it does not decode must refuse it rather than misread the bytes (meTile
+// PR #29: a four-bit decoder fed eight-bit data fails silently).
+bool bits_ok(int fmt, int bits, bool wide_ok) {
+    if (bits == 4) return true;
+    return wide_ok && fmt == Q4_FMT_AFFINE && (bits == 6 || bits == 8);
+}
+
 // Common checks of the W4A8 matmul entry points (pointers checked by callers).
-int matmul_status(int M, int K, int N, int bs, int fmt, int bits) {
-    if (bits != 4) return Q4_ERR_FORMAT;
+// wide_ok: the entry point decodes 6- and 8-bit affine codes.
+int matmul_status(int M, int K, int N, int bs, int fmt, int bits, bool wide_ok = false) {
     if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE) return Q4_ERR_FORMAT;
+    if (!bits_ok(fmt, bits, wide_ok)) return Q4_ERR_FORMAT;
     if (M <= 0 || N <= 0 || K <= 0) return Q4_ERR_DIM;
     return block_status(K, bs, fmt);
 }
@@ -116,29 +126,29 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
 
 int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale, const void* wbias,
             const int8_t* xq, const float* xs, const int32_t* xsum, float* y, void* stream) {
-    int st = matmul_status(M, K, N, bs, fmt, bits);
+    int st = matmul_status(M, K, N, bs, fmt, bits, true);
     if (st) return st;
     // buffer loads address each operand with 32-bit byte offsets
-    if ((long long)M * K >= (1LL << 31) || (long long)N * (K / 2) >= (1LL << 31)) return Q4_ERR_DIM;
+    if ((long long)M * K >= (1LL << 31) || (long long)N * K * bits / 8 >= (1LL << 31)) return Q4_ERR_DIM;
     st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
     if (st) return st;
     // a few rows: stream every weight block once for all of them
     if (M <= q4::GEMM_SMALL_MAX_M)
-        return hip_status(q4::launch_gemm_small(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
+        return hip_status(q4::launch_gemm_small(M, K, N, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
                                                 static_cast<hipStream_t>(stream)));
-    return hip_status(q4::launch_gemm(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
+    return hip_status(q4::launch_gemm(M, K, N, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
                                       static_cast<hipStream_t>(stream)));
 }
 
 int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const int8_t* xq,
                       const int32_t* xsum, int m0, int m1, int32_t* partials, void* stream) {
-    int st = matmul_status(M, K, N, bs, fmt, bits);
+    int st = matmul_status(M, K, N, bs, fmt, bits, path != Q4_PATH_GEMV);
     if (st) return st;
     if (path != Q4_PATH_GEMV && path != Q4_PATH_GEMM && path != Q4_PATH_SMALL) return Q4_ERR_FORMAT;
     if (!wq || !xq || !xsum || !partials) return Q4_ERR_NULL;
     if (!aligned(wq, 16) || !aligned(xq, 16) || !aligned(xsum, 4) || !aligned(partials, 4)) return Q4_ERR_ALIGN;
     if (m0 < 0 || m1 > M || m0 >= m1) return Q4_ERR_RANGE;
-    if ((long long)(m1 - m0) * K >= (1LL << 31) || (long long)N * (K / 2) >= (1LL << 31)) return Q4_ERR_DIM;
+    if ((long long)(m1 - m0) * K >= (1LL << 31) || (long long)N * K * bits / 8 >= (1LL << 31)) return Q4_ERR_DIM;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int ng = K / bs;
     const int8_t* xq0 = xq + (size_t)m0 * K;
@@ -151,11 +161,11 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
     }
     if (path == Q4_PATH_SMALL) {
         if (m1 - m0 > q4::GEMM_SMALL_MAX_M) return Q4_ERR_RANGE;
-        return hip_status(q4::launch_gemm_small(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0,
-                                                nullptr, partials, s));
+        return hip_status(q4::launch_gemm_small(m1 - m0, K, N, bs, fmt, bits, wq, nullptr, nullptr, xq0, nullptr,
+                                                xsum0, nullptr, partials, s));
     }
-    return hip_status(q4::launch_gemm(m1 - m0, K, N, bs, fmt, wq, nullptr, nullptr, xq0, nullptr, xsum0, nullptr,
-                                      partials, s));
+    return hip_status(q4::launch_gemm(m1 - m0, K, N, bs, fmt, bits, wq, nullptr, nullptr, xq0, nullptr, xsum0,
+                                      nullptr, partials, s));
 }
 
 size_t q4_packed_bytes(int K, int N, int bs, int fmt) {
@@ -256,7 +266,8 @@ int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, 
 
 int q4_quantize_weights(int N, int K, int bs, int fmt, int bits, int wdtype, const void* w, uint8_t* wq,
                         void* wscale, void* wbias, void* stream) {
-    if (bits != 4) return Q4_ERR_FORMAT;
+    if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE) return Q4_ERR_FORMAT;
+    if (!bits_ok(fmt, bits, true)) return Q4_ERR_FORMAT;
     if (wdtype != Q4_DT_F32 && wdtype != Q4_DT_BF16) return Q4_ERR_FORMAT;
     if (N <= 0 || K <= 0) return Q4_ERR_DIM;
     int st = block_status(K, bs, fmt);
@@ -265,7 +276,7 @@ int q4_quantize_weights(int N, int K, int bs, int fmt, int bits, int wdtype, con
     if (!aligned(w, wdtype == Q4_DT_F32 ? 4 : 2) || !aligned(wq, 16) || !aligned(wscale, 2) ||
         (wbias && !aligned(wbias, 2)))
         return Q4_ERR_ALIGN;
-    return hip_status(q4::launch_quantize_weights(N, K, bs, fmt, wdtype == Q4_DT_BF16, w, wq, wscale, wbias,
+    return hip_status(q4::launch_quantize_weights(N, K, bs, fmt, bits, wdtype == Q4_DT_BF16, w, wq, wscale, wbias,
                                                   static_cast<hipStream_t>(stream)));
 }
 

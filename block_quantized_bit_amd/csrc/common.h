@@ -65,6 +65,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ uint32_t lo_nibbles(uint32_t w) { return w & 0x0F0F0F0Fu; }
 __device__ __forceinline__ uint32_t hi_nibbles(uint32_t w) { return (w >> 4) & 0x0F0F0F0Fu; }
 
+// 6-bit codes: bytes b = 0..3 of the result take bits 2j and 2j + 1 of byte b
+// of the high-bit plane word w, moved to bits 4 and 5 (the two bits above the
+// code's low nibble).
+__device__ __forceinline__ uint32_t two_bits_high(uint32_t w, int j) { return ((w >> (2 * j)) & 0x03030303u) << 4; }
+
 // Bytes q in 0..15 -> signed bytes q - 8. Adding 0x78 keeps every byte below
 // 0x88 (no carry between bytes); flipping bit 7 then subtracts 128.
 __device__ __forceinline__ uint32_t minus8_bytes(uint32_t q) { return (q + 0x78787878u) ^ 0x80808080u; }

@@ -108,7 +108,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 // block of codes per 128-column tile and stage, rows in order; scales and
 // biases as [tile][group][128]) and xs, xsum are group-major, [K/G][M]. Every
 // staging load of the stage is then contiguous across the workgroup's threads.
-template <int FMT, int G, bool PARTIALS, bool PACKED>
+// BITS: affine code width (MLX PR #4802 serves 4, 6 and 8 bits): 4 -> the
+// nibble planes; 6 -> the nibble planes of the low 4 bits, then at N*K/2 a
+// plane of the high 2 bits (8 bytes per 32-code block: word h holds code
+// 16h + c in byte c % 4, bits 2 * (c / 4)); 8 -> one byte per code, staged as
+// q - 128 (signed for the MFMA) with 128 * s added to the group's bias.
+template <int FMT, int G, bool PARTIALS, bool PACKED, int BITS>
 __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
                                                       const uint16_t* __restrict__ wscale,
                                                       const uint16_t* __restrict__ wbias,
@@ -118,7 +123,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     constexpr int GPS = KS / G;  // blocks or groups per stage
     constexpr int SPG = G / 32;  // MFMA K steps per block or group
     constexpr int A_CH = BM * (KS / 16) / NT;  // 16-byte activation chunks per thread per stage (4)
-    constexpr int B_CH = BN * (KS / 32) / NT;  // 16-byte packed weight chunks per thread per stage (2)
+    constexpr int B_CH = BN * (KS / (BITS == 8 ? 16 : 32)) / NT;  // 16-byte code chunks per thread per stage (2 / 4)
+    static_assert(BITS == 4 || (FMT == 1 && !PACKED && (BITS == 6 || BITS == 8)), "code width");
     constexpr bool AFF = FMT == 1;
     constexpr bool BIAS_MFMA = AFF && !PARTIALS;
     using Sc = Scales<G, FMT>;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     const int ntn = (N + BN - 1) / BN;  // column tiles
     const size_t wrows = PACKED ? (size_t)ntn * BN : (size_t)N;  // weight rows as stored
     const __amdgpu_buffer_rsrc_t r_b =
-        rsrc(wq, (uint32_t)(PACKED ? (size_t)ntn * nstages * (BN * KS / 2) : (size_t)N * (K / 2)));
+        rsrc(wq, (uint32_t)(PACKED ? (size_t)ntn * nstages * (BN * KS / 2) : (size_t)N * K * BITS / 8));
     const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
     const __amdgpu_buffer_rsrc_t r_xsum = rsrc(xsum, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
     const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, PARTIALS ? 0u : (uint32_t)(wrows * ngroups * 2));
@@ -156,9 +162,21 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
+        if (BITS == 8) {  // row c = idx / 8, 16-byte chunk idx % 8 of the stage's 128 codes
+            const int idx = tid + NT * i, c = idx >> 3, c16 = idx & 7;
+            off_b[i] = (n0 + c < N) ? (uint32_t)((n0 + c) * K + c16 * 16) : OUT;
+        } else {
+            const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
+            // packed: row c's 64 bytes of the stage sit at c * 64 of the tile's block
+            off_b[i] = PACKED ? (uint32_t)(idx * 16) : (n0 + c < N) ? (uint32_t)((n0 + c) * (K / 2) + b * 16) : OUT;
+        }
+    }
+    // 6 bits: the high 2-bit plane of each 32-code block, 8 bytes per block
+    uint32_t off_p[B_CH];
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
         const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
-        // packed: row c's 64 bytes of the stage sit at c * 64 of the tile's block
-        off_b[i] = PACKED ? (uint32_t)(idx * 16) : (n0 + c < N) ? (uint32_t)((n0 + c) * (K / 2) + b * 16) : OUT;
+        off_p[i] = (BITS == 6 && n0 + c < N) ? (uint32_t)((size_t)N * (K / 2) + (n0 + c) * (K / 4) + b * 8) : OUT;
     }
     // scale staging: the thread covers (gi, r) = divmod(tid + NT*i, 128) of the
     // GPS*128 activation scales and of the GPS*128 weight scales
@@ -180,6 +198,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     }
 
     uint4 ra[A_CH], rb[B_CH];
+    uint2 rp[BITS == 6 ? B_CH : 1];
     float rxs[SC_N];
     int32_t rxsum[SC_N];
     uint32_t rws[SC_N], rwb[SC_N];
@@ -199,10 +218,14 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
-            const int b = (tid + NT * i) & 3;
-            const uint32_t o = (b * 32 < ks) ? off_b[i] : OUT;
-            const int sb = PACKED ? (tn * nstages + st) * (BN * KS / 2) : (k0 >> 1);
+            // the chunk's first k within the stage: 16 * (idx % 8) for 8 bits, 32 * (idx % 4) otherwise
+            const int kc = BITS == 8 ? 16 * ((tid + NT * i) & 7) : 32 * ((tid + NT * i) & 3);
+            const uint32_t o = (kc < ks) ? off_b[i] : OUT;
+            const int sb = PACKED ? (tn * nstages + st) * (BN * KS / 2) : (BITS == 8 ? k0 : (k0 >> 1));
             rb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_b, o, sb, 0));
+            if (BITS == 6)
+                rp[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r_b, (kc < ks) ? off_p[i] : OUT,
+                                                                                        k0 >> 2, 0));
         }
         if (!PARTIALS) {
             const int g0 = k0 / G;
@@ -229,12 +252,25 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
+            if (BITS == 8) {  // codes q - 128 as signed bytes: flip bit 7 of every byte
+                const int idx = tid + NT * i, c = idx >> 3, c16 = idx & 7;
+                const uint4 v = rb[i];
+                T.b[swz(c, c16)] = make_uint4(v.x ^ 0x80808080u, v.y ^ 0x80808080u, v.z ^ 0x80808080u,
+                                              v.w ^ 0x80808080u);
+                continue;
+            }
             const int idx = tid + NT * i, c = idx >> 2, b = idx & 3;
             uint4 lo = make_uint4(lo_nibbles(rb[i].x), lo_nibbles(rb[i].y), lo_nibbles(rb[i].z), lo_nibbles(rb[i].w));
             uint4 hi = make_uint4(hi_nibbles(rb[i].x), hi_nibbles(rb[i].y), hi_nibbles(rb[i].z), hi_nibbles(rb[i].w));
             if (FMT == 0) {
                 lo = make_uint4(minus8_bytes(lo.x), minus8_bytes(lo.y), minus8_bytes(lo.z), minus8_bytes(lo.w));
                 hi = make_uint4(minus8_bytes(hi.x), minus8_bytes(hi.y), minus8_bytes(hi.z), minus8_bytes(hi.w));
+            }
+            if (BITS == 6) {  // word j of a half takes bits 2j, 2j+1 of every byte of its plane word
+                lo = make_uint4(lo.x | two_bits_high(rp[i].x, 0), lo.y | two_bits_high(rp[i].x, 1),
+                                lo.z | two_bits_high(rp[i].x, 2), lo.w | two_bits_high(rp[i].x, 3));
+                hi = make_uint4(hi.x | two_bits_high(rp[i].y, 0), hi.y | two_bits_high(rp[i].y, 1),
+                                hi.z | two_bits_high(rp[i].y, 2), hi.w | two_bits_high(rp[i].y, 3));
             }
             T.b[swz(c, 2 * b)] = lo;      // k = 32b .. 32b+15
             T.b[swz(c, 2 * b + 1)] = hi;  // k = 32b+16 .. 32b+31
@@ -247,7 +283,8 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
                 S.ws[gi][r] = AFF ? bf16_to_float(rws[i]) : half_to_float(rws[i]);
                 if (AFF) {
                     S.xb[gi][r] = rxs[i] * (float)rxsum[i];
-                    S.wb[gi][r] = bf16_to_float(rwb[i]);
+                    // 8 bits: the MFMA sees q - 128, so the bias term carries 128 * s
+                    S.wb[gi][r] = bf16_to_float(rwb[i]) + (BITS == 8 ? 128.0f * bf16_to_float(rws[i]) : 0.0f);
                 }
             }
         }
@@ -305,10 +342,16 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
             const int mb = m0 + xrow + 32 * i;
             const size_t rstride = (size_t)__builtin_amdgcn_readfirstlane(N * ngroups);
             int32_t* pb = partials + ((size_t)mb * N + n) * ngroups + g;
+            const size_t sstride = (size_t)__builtin_amdgcn_readfirstlane(ngroups);
+            const int32_t* sb = xsum + (size_t)mb * ngroups + g;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int dr = 8 * (r >> 2) + (r & 3);
-                if (mb + dr < M && n < N && g < ngroups) pb[dr * rstride] = d[r];
+                if (mb + dr < M && n < N && g < ngroups) {
+                    // 8 bits: the MFMA summed (q - 128) * xq; the reported partial is sum q * xq
+                    const int fix = BITS == 8 ? 128 * sb[dr * sstride] : 0;
+                    pb[dr * rstride] = d[r] + fix;
+                }
             }
             return;
         }
@@ -439,7 +482,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_kernel(int M, int K, int N, const 
     }
 }
 
-template <int FMT, int G, bool PACKED>
+template <int FMT, int G, bool PACKED, int BITS = 4>
 hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                       hipStream_t stream) {
@@ -447,7 +490,7 @@ hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale
     const size_t lds = 2 * sizeof(Tiles) + RING * sizeof(Scales<G, FMT>);
     const uint16_t* ws = static_cast<const uint16_t*>(wscale);
     const uint16_t* wb = static_cast<const uint16_t*>(wbias);
-    auto k = partials ? gemm_kernel<FMT, G, true, PACKED> : gemm_kernel<FMT, G, false, PACKED>;
+    auto k = partials ? gemm_kernel<FMT, G, true, PACKED, BITS> : gemm_kernel<FMT, G, false, PACKED, BITS>;
     static bool attr[2] = {false, false};
     if (!attr[partials != nullptr]) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -489,12 +532,25 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(int N, int ngroups, co
 
 }  // namespace
 
-hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+template <int G>
+hipError_t launch_affine_bits(int bits, int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
+                              const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
+                              hipStream_t stream) {
+    if (bits == 4) return launch_fmt<1, G, false, 4>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bits == 6) return launch_fmt<1, G, false, 6>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bits == 8) return launch_fmt<1, G, false, 8>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
                        const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                        int32_t* partials, hipStream_t stream) {
-    if (fmt == 0) return launch_fmt<0, 32, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (bs == 64) return launch_fmt<1, 64, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (bs == 128) return launch_fmt<1, 128, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (fmt == 0) {
+        if (bits != 4) return hipErrorInvalidValue;
+        return launch_fmt<0, 32, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    }
+    if (bs == 64) return launch_affine_bits<64>(bits, M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bs == 128) return launch_affine_bits<128>(bits, M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
     return hipErrorInvalidValue;
 }
 

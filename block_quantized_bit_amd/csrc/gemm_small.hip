@@ -51,18 +51,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
 }
 
-template <int G, int MT>
+// Code bytes per weight row and chunk: the main part (nibbles, or bytes for
+// 8-bit codes) and, for 6-bit codes, the high 2-bit plane after it.
+template <int MT, int BITS>
+constexpr int main_bytes() { return BITS == 8 ? chunk_k<MT>() : chunk_k<MT>() / 2; }
+template <int MT, int BITS>
+constexpr int plane_bytes() { return BITS == 6 ? chunk_k<MT>() / 4 : 0; }
+
+template <int G, int MT, int BITS>
 struct SmallLds {
     static constexpr int KC = chunk_k<MT>();
     static constexpr int GPC = KC / G;  // groups per chunk
-    uint8_t w[SN][KC / 2 + 16];         // packed codes of the chunk (16 bytes of padding per row)
+    uint8_t w[SN][main_bytes<MT, BITS>() + plane_bytes<MT, BITS>() + 16];  // codes (16 bytes of padding per row)
     uint8_t a[16 * MT][KC + 16];        // activation codes of the chunk
     float xs[GPC][16 * MT];             // activation scales, group-major
     float xb[GPC][16 * MT];             // xs * xsum (affine)
     float red[SW][MT][256];             // per-wavefront partial sums
 };
 
-template <int FMT, int G, int MT, bool PARTIALS>
+// BITS: affine code width, 4, 6 or 8 (layouts as in the tiled GEMM); 8-bit
+// codes enter the MFMA as q - 128 with 128 * s added to the group's bias.
+template <int FMT, int G, int MT, bool PARTIALS, int BITS>
 __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
                                                             const uint16_t* __restrict__ wscale,
                                                             const uint16_t* __restrict__ wbias,
@@ -73,12 +82,15 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
     constexpr int SPG = G / 32;     // MFMA steps per block or group
     constexpr bool AFF = FMT == 1;
     constexpr int MR = 16 * MT;     // rows covered by the MFMA tiles
-    using L = SmallLds<G, MT>;
+    using L = SmallLds<G, MT, BITS>;
+    constexpr int MB = main_bytes<MT, BITS>(), PB = plane_bytes<MT, BITS>();
     constexpr int KC = L::KC;
     constexpr int GPC = L::GPC;
     constexpr int SPW = KC / 32 / SW;  // MFMA steps per wavefront per chunk
     static_assert(SPW % SPG == 0, "a wavefront's share of a chunk holds whole groups");
-    constexpr int W_CH = SN * (KC / 2) / 16 / SNT;     // 16-byte weight loads per thread per chunk (2)
+    constexpr int W_CH = SN * MB / 16 / SNT;           // 16-byte code loads per thread per chunk
+    constexpr int P_CH = (SN * PB / 16 + SNT - 1) / SNT;  // 16-byte high-plane loads (6 bits)
+    constexpr int CPS = BITS == 8 ? 16 : 32;           // codes per 16 bytes of the main part
     constexpr int A_CH = MR * KC / 16 / SNT;           // 16-byte activation loads per thread per chunk (4 / 8)
     constexpr int S_CH = (MR * GPC + SNT - 1) / SNT;   // scale values per thread per chunk
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -90,7 +102,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
     const int ngroups = K / G;
     const int nchunks = (K + KC - 1) / KC;
 
-    const __amdgpu_buffer_rsrc_t r_b = rsrc(wq, (uint32_t)((size_t)N * (K / 2)));
+    const __amdgpu_buffer_rsrc_t r_b = rsrc(wq, (uint32_t)((size_t)N * K * BITS / 8));
     const __amdgpu_buffer_rsrc_t r_a = rsrc(xq, (uint32_t)((size_t)M * K));
     const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)((size_t)M * ngroups * 4));
     const __amdgpu_buffer_rsrc_t r_xsum = rsrc(xsum, (PARTIALS || !AFF) ? 0u : (uint32_t)((size_t)M * ngroups * 4));
@@ -105,7 +117,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
     // biases) of its column for the groups its wavefront will rescale.
     constexpr int GPW = SPW / SPG;  // groups per wavefront per chunk
     const uint32_t os = (n0 + c < N) ? (uint32_t)((n0 + c) * ngroups * 2) : OUT;  // this lane's weight-scale row
-    uint4 rw[2][W_CH], ra[2][A_CH];
+    uint4 rw[2][W_CH], rpl[2][P_CH > 0 ? P_CH : 1], ra[2][A_CH];
     float rxs[2][S_CH], rxb[2][S_CH];
     uint32_t rws[2][GPW], rwb[2][GPW];
     auto load_chunk = [&](int ch, auto setc) {
@@ -113,10 +125,18 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
         const int k0 = ch * KC;
 #pragma unroll
         for (int i = 0; i < W_CH; ++i) {
-            const int idx = tid + SNT * i, r = idx / (KC / 32), seg = idx % (KC / 32);  // 16-byte segment
-            const bool in = n0 + r < N && k0 + 32 * seg < K;
+            const int idx = tid + SNT * i, r = idx / (MB / 16), seg = idx % (MB / 16);  // 16-byte segment
+            const bool in = n0 + r < N && k0 + CPS * seg < K;
+            const uint32_t rowb = BITS == 8 ? (uint32_t)K : (uint32_t)(K / 2);
             rw[B][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                r_b, in ? (uint32_t)((n0 + r) * (K / 2) + 16 * seg) : OUT, k0 / 2, 0));
+                r_b, in ? (uint32_t)((n0 + r) * rowb + 16 * seg) : OUT, BITS == 8 ? k0 : k0 / 2, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < P_CH; ++i) {  // 16 bytes of the high plane hold 64 codes
+            const int idx = tid + SNT * i, r = idx / (PB / 16), seg = idx % (PB / 16);
+            const bool in = idx < SN * PB / 16 && n0 + r < N && k0 + 64 * seg < K;
+            const uint32_t o = (uint32_t)((size_t)N * (K / 2) + (size_t)(n0 + r) * (K / 4) + 16 * seg);
+            rpl[B][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_b, in ? o : OUT, k0 / 4, 0));
         }
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
@@ -148,8 +168,13 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
         constexpr int B = decltype(setc)::value;
 #pragma unroll
         for (int i = 0; i < W_CH; ++i) {
-            const int idx = tid + SNT * i, r = idx / (KC / 32), seg = idx % (KC / 32);
+            const int idx = tid + SNT * i, r = idx / (MB / 16), seg = idx % (MB / 16);
             *reinterpret_cast<uint4*>(&S.w[r][16 * seg]) = rw[B][i];
+        }
+#pragma unroll
+        for (int i = 0; i < P_CH; ++i) {
+            const int idx = tid + SNT * i, r = idx / (PB / 16), seg = idx % (PB / 16);
+            if (idx < SN * PB / 16) *reinterpret_cast<uint4*>(&S.w[r][MB + 16 * seg]) = rpl[B][i];
         }
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
@@ -197,11 +222,24 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
 #pragma unroll
             for (int e = 0; e < SPG; ++e) {
                 const int sl = wave * SPW + u * SPG + e;  // step within the chunk
-                const uint2 wv = *reinterpret_cast<const uint2*>(&S.w[c][16 * sl + 8 * (q & 1)]);
-                uint32_t lo = (wv.x >> shift) & 0x0F0F0F0Fu, hi = (wv.y >> shift) & 0x0F0F0F0Fu;
-                if (FMT == 0) {
-                    lo = minus8_bytes(lo);
-                    hi = minus8_bytes(hi);
+                uint32_t lo, hi;
+                if (BITS == 8) {  // this lane's 8 codes are bytes 8q .. 8q+7 of the step: q - 128
+                    const uint2 wv = *reinterpret_cast<const uint2*>(&S.w[c][32 * sl + 8 * q]);
+                    lo = wv.x ^ 0x80808080u;
+                    hi = wv.y ^ 0x80808080u;
+                } else {
+                    const uint2 wv = *reinterpret_cast<const uint2*>(&S.w[c][16 * sl + 8 * (q & 1)]);
+                    lo = (wv.x >> shift) & 0x0F0F0F0Fu;
+                    hi = (wv.y >> shift) & 0x0F0F0F0Fu;
+                    if (FMT == 0) {
+                        lo = minus8_bytes(lo);
+                        hi = minus8_bytes(hi);
+                    }
+                    if (BITS == 6) {  // word q / 2 of the step's plane; codes 8(q&1) .. +7 take bit pairs 2(q&1), +1
+                        const uint32_t pw = *reinterpret_cast<const uint32_t*>(&S.w[c][MB + 8 * sl + 4 * (q >> 1)]);
+                        lo |= two_bits_high(pw, 2 * (q & 1));
+                        hi |= two_bits_high(pw, 2 * (q & 1) + 1);
+                    }
                 }
                 const long bop = (long)(((uint64_t)hi << 32) | lo);
 #pragma unroll
@@ -220,7 +258,10 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const int m = 16 * t + 4 * q + r;
-                            if (m < M) partials[((size_t)m * N + n) * ngroups + g] = P[t][r];
+                            // 8 bits: the MFMA summed (q - 128) * xq; the reported partial is sum q * xq
+                            if (m < M)
+                                partials[((size_t)m * N + n) * ngroups + g] =
+                                    P[t][r] + (BITS == 8 ? 128 * xsum[(size_t)m * ngroups + g] : 0);
                         }
                 }
                 continue;
@@ -228,7 +269,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
             // groups past K have zero codes and zero scales and biases
             const int gi = wave * GPW + u;  // group within the chunk
             const float w = AFF ? bf16_to_float(wsb[u]) : half_to_float(wsb[u]);
-            const float b = AFF ? bf16_to_float(wbb[u]) : 0.0f;
+            const float b = AFF ? bf16_to_float(wbb[u]) + (BITS == 8 ? 128.0f * w : 0.0f) : 0.0f;
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 const float4 xv = *reinterpret_cast<const float4*>(&S.xs[gi][16 * t + 4 * q]);
@@ -274,12 +315,12 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
     }
 }
 
-template <int FMT, int G, int MT>
+template <int FMT, int G, int MT, int BITS>
 hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                      const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                      hipStream_t stream) {
-    const size_t lds = sizeof(SmallLds<G, MT>);
-    auto k = partials ? gemm_small_kernel<FMT, G, MT, true> : gemm_small_kernel<FMT, G, MT, false>;
+    const size_t lds = sizeof(SmallLds<G, MT, BITS>);
+    auto k = partials ? gemm_small_kernel<FMT, G, MT, true, BITS> : gemm_small_kernel<FMT, G, MT, false, BITS>;
     static bool attr[2] = {false, false};
     if (lds > 64 * 1024 && !attr[partials != nullptr]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -293,23 +334,36 @@ hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale,
     return hipGetLastError();
 }
 
-template <int FMT, int G>
+template <int FMT, int G, int BITS = 4>
 hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                       hipStream_t stream) {
-    if (M <= 16) return launch_mt<FMT, G, 1>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    return launch_mt<FMT, G, 2>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (M <= 16) return launch_mt<FMT, G, 1, BITS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return launch_mt<FMT, G, 2, BITS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+}
+
+template <int G>
+hipError_t launch_affine_bits(int bits, int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
+                              const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
+                              hipStream_t stream) {
+    if (bits == 4) return launch_fmt<1, G, 4>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bits == 6) return launch_fmt<1, G, 6>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bits == 8) return launch_fmt<1, G, 8>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream) {
     if (M < 1 || M > GEMM_SMALL_MAX_M) return hipErrorInvalidValue;
-    if (fmt == 0) return launch_fmt<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (bs == 64) return launch_fmt<1, 64>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (bs == 128) return launch_fmt<1, 128>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (fmt == 0) {
+        if (bits != 4) return hipErrorInvalidValue;
+        return launch_fmt<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    }
+    if (bs == 64) return launch_affine_bits<64>(bits, M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bs == 128) return launch_affine_bits<128>(bits, M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
     return hipErrorInvalidValue;
 }
 

@@ -25,7 +25,8 @@ hipError_t launch_gemv_fused(int K, int N, int bs, int fmt, bool xbf16, const vo
                              const void* wscale, const void* wbias, float* y, int8_t* xq_out, float* xs_out,
                              int32_t* xsum_out, hipStream_t stream);
 
-hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+// bits: code width of affine weights (4, 6 or 8; Q4_0 is 4-bit only).
+hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
                        const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                        int32_t* partials, hipStream_t stream);
 
@@ -33,7 +34,7 @@ hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq, 
 // for all rows (16x16x32 int8 MFMA, K chunks staged in LDS and split over the
 // wavefronts of a workgroup). Same arguments as launch_gemm.
 constexpr int GEMM_SMALL_MAX_M = 32;
-hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream);
 
@@ -55,7 +56,7 @@ hipError_t launch_backward(int M, int K, int N, int fmt, int bs, const uint8_t* 
 hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
 hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
 
-hipError_t launch_quantize_weights(int N, int K, int bs, int fmt, bool bf16, const void* w, uint8_t* wq,
+hipError_t launch_quantize_weights(int N, int K, int bs, int fmt, int bits, bool bf16, const void* w, uint8_t* wq,
                                    void* wscale, void* wbias, hipStream_t stream);
 hipError_t launch_q4k_quantize_weights(int N, int K, const float* w, void* blocks, hipStream_t stream);
 

@@ -62,10 +62,17 @@ __global__ __launch_bounds__(256) void quantize_q4_0_kernel(long long nblocks, i
     wd[b] = d16;
 }
 
-template <int G, bool BF16>
+// Affine codes 0 .. 2^BITS - 1 (MLX PR #4802 serves 4, 6 and 8 bits). Layouts:
+// BITS 4: the nibble planes above; BITS 8: one byte per code; BITS 6: the low
+// 4 bits in the 4-bit layout, then at plane_off the high 2 bits, 8 bytes per
+// 32-code block: word h holds code 16h + c of the block in byte c % 4, bits
+// 2 * (c / 4) and 2 * (c / 4) + 1.
+template <int G, bool BF16, int BITS>
 __global__ __launch_bounds__(256) void quantize_affine_kernel(long long ngroups_total, int K,
                                                               const void* __restrict__ w, uint8_t* __restrict__ wq,
-                                                              uint16_t* __restrict__ ws, uint16_t* __restrict__ wb) {
+                                                              uint16_t* __restrict__ ws, uint16_t* __restrict__ wb,
+                                                              size_t plane_off) {
+    constexpr int QMAX = (1 << BITS) - 1;
     const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (g >= ngroups_total) return;
     const size_t base = (size_t)g * G;
@@ -76,29 +83,46 @@ __global__ __launch_bounds__(256) void quantize_affine_kernel(long long ngroups_
         mx = fmaxf(mx, v);
     }
     const float range = mx - mn;
-    const uint16_t s16 = float_to_bf16_bits(range / 15.0f);
+    const uint16_t s16 = float_to_bf16_bits(range / (float)QMAX);
     const uint16_t b16 = float_to_bf16_bits(mn);
     const float s = bf16_to_float(s16), bias = bf16_to_float(b16);
+    auto code = [&](int j) {
+        if (s == 0.0f) return 0;
+        const float t = load_w<BF16>(w, base + j) - bias;
+        return min(QMAX, max(0, (int)rintf(t / s)));
+    };
     for (int blk = 0; blk < G / 32; ++blk) {
-        uint32_t out[4];
+        if (BITS == 8) {
+            uint32_t out[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb) word |= (uint32_t)code(32 * blk + 4 * t + bb) << (8 * bb);
+                out[t] = word;
+            }
+            uint4* dst = reinterpret_cast<uint4*>(wq + base + 32 * blk);
+            dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+            dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+            continue;
+        }
+        uint32_t out[4], hp[2] = {0u, 0u};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             uint32_t word = 0;
 #pragma unroll
             for (int bb = 0; bb < 4; ++bb) {
-                const int jl = 32 * blk + 4 * t + bb;
-                int ql = 0, qh = 0;
-                if (s != 0.0f) {
-                    const float tl = load_w<BF16>(w, base + jl) - bias;
-                    const float th = load_w<BF16>(w, base + jl + 16) - bias;
-                    ql = min(15, max(0, (int)rintf(tl / s)));
-                    qh = min(15, max(0, (int)rintf(th / s)));
+                const int ql = code(32 * blk + 4 * t + bb), qh = code(32 * blk + 16 + 4 * t + bb);
+                word |= (uint32_t)((ql & 15) | ((qh & 15) << 4)) << (8 * bb);
+                if (BITS == 6) {  // codes 4t + bb and 16 + 4t + bb: byte bb, bits 2t of words 0 and 1
+                    hp[0] |= (uint32_t)(ql >> 4) << (8 * bb + 2 * t);
+                    hp[1] |= (uint32_t)(qh >> 4) << (8 * bb + 2 * t);
                 }
-                word |= (uint32_t)(ql | (qh << 4)) << (8 * bb);
             }
             out[t] = word;
         }
         *reinterpret_cast<uint4*>(wq + base / 2 + 16 * blk) = make_uint4(out[0], out[1], out[2], out[3]);
+        if (BITS == 6) *reinterpret_cast<uint2*>(wq + plane_off + base / 4 + 8 * blk) = make_uint2(hp[0], hp[1]);
     }
     ws[g] = s16;
     wb[g] = b16;
@@ -159,27 +183,46 @@ __global__ __launch_bounds__(256) void quantize_q4k_kernel(long long nsb_total, 
     }
 }
 
+template <int G, int BITS>
+hipError_t launch_affine(long long nb, int K, bool bf16, const void* w, uint8_t* wq, uint16_t* ws, uint16_t* wb,
+                         size_t plane_off, hipStream_t stream) {
+    const unsigned grid = (unsigned)((nb + 255) / 256);
+    if (bf16)
+        hipLaunchKernelGGL((quantize_affine_kernel<G, true, BITS>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws,
+                           wb, plane_off);
+    else
+        hipLaunchKernelGGL((quantize_affine_kernel<G, false, BITS>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq,
+                           ws, wb, plane_off);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_affine_bits(int bits, long long nb, int K, bool bf16, const void* w, uint8_t* wq, uint16_t* ws,
+                              uint16_t* wb, size_t plane_off, hipStream_t stream) {
+    if (bits == 4) return launch_affine<G, 4>(nb, K, bf16, w, wq, ws, wb, plane_off, stream);
+    if (bits == 6) return launch_affine<G, 6>(nb, K, bf16, w, wq, ws, wb, plane_off, stream);
+    if (bits == 8) return launch_affine<G, 8>(nb, K, bf16, w, wq, ws, wb, plane_off, stream);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-hipError_t launch_quantize_weights(int N, int K, int bs, int fmt, bool bf16, const void* w, uint8_t* wq,
+hipError_t launch_quantize_weights(int N, int K, int bs, int fmt, int bits, bool bf16, const void* w, uint8_t* wq,
                                    void* wscale, void* wbias, hipStream_t stream) {
     const long long nb = (long long)N * (K / bs);
     const unsigned grid = (unsigned)((nb + 255) / 256);
     uint16_t* ws = static_cast<uint16_t*>(wscale);
     uint16_t* wb = static_cast<uint16_t*>(wbias);
+    const size_t plane_off = (size_t)N * (K / 2);  // 6-bit: the high 2-bit plane follows the nibble planes
     if (fmt == 0) {
+        if (bits != 4) return hipErrorInvalidValue;
         if (bf16) hipLaunchKernelGGL((quantize_q4_0_kernel<true>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws);
         else hipLaunchKernelGGL((quantize_q4_0_kernel<false>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws);
-    } else if (bs == 64) {
-        if (bf16) hipLaunchKernelGGL((quantize_affine_kernel<64, true>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws, wb);
-        else hipLaunchKernelGGL((quantize_affine_kernel<64, false>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws, wb);
-    } else if (bs == 128) {
-        if (bf16) hipLaunchKernelGGL((quantize_affine_kernel<128, true>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws, wb);
-        else hipLaunchKernelGGL((quantize_affine_kernel<128, false>), dim3(grid), dim3(256), 0, stream, nb, K, w, wq, ws, wb);
-    } else {
-        return hipErrorInvalidValue;
+        return hipGetLastError();
     }
-    return hipGetLastError();
+    if (bs == 64) return launch_affine_bits<64>(bits, nb, K, bf16, w, wq, ws, wb, plane_off, stream);
+    if (bs == 128) return launch_affine_bits<128>(bits, nb, K, bf16, w, wq, ws, wb, plane_off, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_q4k_quantize_weights(int N, int K, const float* w, void* blocks, hipStream_t stream) {

@@ -66,6 +66,20 @@ def test_matmul_validation(entry, kw, status):
     assert getattr(q4.lib(), entry)(*args) == status
 
 
+@pytest.mark.parametrize("entry", ["q4_gemv", "q4_gemm"])
+def test_code_width_guard(entry):
+    # meTile PR #29: a decoder handed a width it does not decode must refuse it. Q4_0 is 4-bit only; the decode
+    # GEMV decodes 4-bit codes only; widths other than 4, 6, 8 are refused everywhere (all before any launch).
+    f = getattr(q4.lib(), entry)
+    for bits in (2, 3, 5, 7, 16):
+        assert f(*gemm_args(M=1, fmt=1, bs=64, wb=A, bits=bits)) == FORMAT
+    assert f(*gemm_args(M=1, fmt=0, bits=8)) == FORMAT
+    assert f(*gemm_args(M=1, fmt=0, bits=6)) == FORMAT
+    if entry == "q4_gemv":
+        assert f(*gemm_args(M=1, fmt=1, bs=64, wb=A, bits=8)) == FORMAT
+        assert f(*gemm_args(M=1, fmt=1, bs=64, wb=A, bits=6)) == FORMAT
+
+
 def test_gemv_requires_one_row():
     assert q4.lib().q4_gemv(*gemm_args(M=2)) == DIM
 
@@ -180,7 +194,8 @@ def test_q4k_validation():
 
 def test_weight_quantizer_validation():
     f = q4.lib().q4_quantize_weights
-    assert f(8, 128, 32, 0, 8, 0, A, A, A, None, None) == FORMAT
+    assert f(8, 128, 32, 0, 8, 0, A, A, A, None, None) == FORMAT      # Q4_0 is 4-bit only
+    assert f(8, 128, 64, 1, 5, 0, A, A, A, None, None) == FORMAT      # affine: 4, 6 or 8 bits
     assert f(8, 128, 32, 0, 4, 3, A, A, A, None, None) == FORMAT
     assert f(8, 128, 64, 1, 4, 1, A, A, A, None, None) == NULL
     assert f(8, 100, 32, 0, 4, 0, A, A, A, None, None) == BLOCK

@@ -377,6 +377,72 @@ def test_small_gemm_deterministic():
     assert torch.equal(y1, y2)
 
 
+# ---------------------------------------------------------------- affine 6- and 8-bit codes
+
+def _bits_case(bits, g, M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w16 = synth.bf16_bits((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    wq, ws, wb = oracle.quantize_affine(w16, g, bits)
+    return w16, (wq, ws, wb), oracle.quantize_act(x, g)
+
+
+BITS_CASES = [(6, 64, 3, 320, 37), (6, 128, 130, 384, 131), (6, 64, 17, 4096, 65), (8, 64, 2, 192, 33),
+              (8, 128, 129, 512, 257), (8, 64, 32, 4096, 48), (8, 128, 200, 1152, 64)]
+
+
+@pytest.mark.parametrize("bits,g", [(6, 64), (6, 128), (8, 64), (8, 128)])
+def test_quantize_weights_bits_bit_exact(bits, g):
+    print(f"case quantize affine {bits}-bit g={g}", flush=True)
+    w16, (wq, ws, wb), _ = _bits_case(bits, g, 1, 1024, 77, bits * g)
+    gq, gs, gb = q4.quantize_weights(to_dev(w16, torch.bfloat16), "affine", g, bits=bits)
+    _sync()
+    assert np.array_equal(to_np(gq).reshape(-1), wq.reshape(-1))
+    assert np.array_equal(to_np(gs), ws) and np.array_equal(to_np(gb), wb)
+
+
+@pytest.mark.parametrize("bits,g,M,K,N", BITS_CASES)
+def test_bits_partials_bit_exact(bits, g, M, K, N):
+    print(f"case partials {bits}-bit g={g} M={M} K={K} N={N}", flush=True)
+    _, (wq, ws, wb), act = _bits_case(bits, g, M, K, N, M + K + N + bits)
+    ref = oracle.q4_partials(wq, act[0], K, N, g, FMT["affine"], bits=bits)
+    args = (to_dev(wq), to_dev(act[0]), to_dev(act[2]))
+    got = q4.debug_partials("gemm", "affine", g, *args, bits=bits)
+    _sync()
+    assert np.array_equal(to_np(got), ref)
+    if M <= 32:
+        gs_ = q4.debug_partials("small", "affine", g, *args, bits=bits)
+        _sync()
+        assert np.array_equal(to_np(gs_), ref)
+
+
+@pytest.mark.parametrize("bits,g,M,K,N", BITS_CASES)
+def test_bits_gemm_ragged(bits, g, M, K, N):
+    print(f"case gemm {bits}-bit g={g} M={M} K={K} N={N}", flush=True)
+    _, (wq, ws, wb), act = _bits_case(bits, g, M, K, N, 3 * M + K + N + bits)
+    y = q4.gemm("affine", g, to_dev(wq), to_dev(ws, torch.bfloat16), to_dev(wb, torch.bfloat16),
+                *[to_dev(a) for a in act], bits=bits)
+    _sync()
+    ref = oracle.q4_gemm(wq, ws, wb, *act, K, N, g, FMT["affine"], bits=bits)
+    assert rel_rms(to_np(y), ref) <= TOL
+
+
+@pytest.mark.parametrize("bits,g", [(6, 64), (8, 64), (8, 128)])
+def test_bits_gemm_workload_sampled(bits, g):
+    # the M=1024, K=N=4096 bf16 workload with its weights quantized at 6 or 8 bits
+    print(f"case gemm {bits}-bit g={g} 1024x4096x4096 sampled", flush=True)
+    wl, x, w16, _, _ = workload_data("affine_g64_1024x4096x4096")
+    wq, ws, wb = oracle.quantize_affine(w16, g, bits)
+    gq, gs, gsum = q4.quantize_act(to_dev(x), g)
+    y = q4.gemm("affine", g, to_dev(wq), to_dev(ws, torch.bfloat16), to_dev(wb, torch.bfloat16), gq, gs, gsum,
+                bits=bits)
+    _sync()
+    act = (to_np(gq), to_np(gs), to_np(gsum))
+    ms, ns = sample_pairs(wl.M, wl.N, 1500, bits * 100 + g)
+    ref = oracle.q4_gemm_sample(wq, ws, wb, *act, wl.K, wl.N, g, FMT["affine"], ms, ns, bits=bits)
+    assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
+
+
 # ---------------------------------------------------------------- packed weights, fused quantize + GEMM
 
 def _pack_reference(wq, ws, wb, K, N, bs):
