@@ -29,17 +29,27 @@
  *   - Errors: an invalid call returns a nonzero q4_status and enqueues
  *     nothing. Q4_ERR_HIP reports a failed kernel launch. q4_status_string()
  *     names a status.
- *   - Bit width: `bits` must be 4. Any other value is rejected with
- *     Q4_ERR_FORMAT: these kernels decode two codes per byte, and a wider
- *     format passed to them would be decoded wrongly without any other sign
- *     (meTile PR #29, "Measure the int8 multi-row headroom, and keep the
- *     four-bit guard that was protecting us").
+ *   - Bit width: `bits` is the code width. Q4_0 codes are 4 bits. Affine
+ *     codes may be 4, 6 or 8 bits wide (MLX PR #4802 serves all three on its
+ *     int8 path) in q4_gemm, q4_debug_partials (GEMM paths) and
+ *     q4_quantize_weights; every other entry point decodes 4-bit codes only.
+ *     A width an entry point does not decode is rejected with Q4_ERR_FORMAT
+ *     before any launch: a decoder handed another width reads the bytes
+ *     wrongly without any other sign (meTile PR #29, "Measure the int8
+ *     multi-row headroom, and keep the four-bit guard that was protecting us").
  *
- * Packed weight layout (shared by Q4_0 and affine)
- *   wq [N][K/2] bytes. Block b (32 weights) of row n is the 16 bytes at
- *   wq + n*K/2 + 16*b; byte j holds the code of k = 32*b + j in its low nibble
- *   and of k = 32*b + 16 + j in its high nibble. An affine group of g weights
- *   is g/32 consecutive blocks.
+ * Code layout (shared by Q4_0 and affine)
+ *   4 bits: wq [N][K/2] bytes. Block b (32 weights) of row n is the 16 bytes
+ *   at wq + n*K/2 + 16*b; byte j holds the code of k = 32*b + j in its low
+ *   nibble and of k = 32*b + 16 + j in its high nibble. An affine group of g
+ *   weights is g/32 consecutive blocks.
+ *   8 bits (affine): wq [N][K] bytes, byte k of row n is the code of k.
+ *   6 bits (affine): N*K*3/4 bytes. The low 4 bits of every code in the
+ *   4-bit layout (N*K/2 bytes), then the high 2 bits: N*K/4 bytes, row n at
+ *   N*K/2 + n*K/4, block b at 8*b within it as two little-endian 32-bit
+ *   words; word h holds code 32*b + 16*h + c (c = 0..15) in byte c % 4, bits
+ *   2*(c/4) and 2*(c/4) + 1.
+ *   Affine codes of width B run 0 .. 2^B - 1; the weight is s*q + b.
  *
  * Q4_K block layout (144 bytes, 4.5 bits per weight)
  *   { fp16 d; fp16 dmin; uint8 scales[12]; uint8 qs[128]; }, blocks [N][K/256].
@@ -65,7 +75,7 @@ typedef enum {
     Q4_ERR_NULL = 1,     /* a required pointer is NULL */
     Q4_ERR_DIM = 2,      /* M, N or K out of range (<= 0, or an entry point's limit) */
     Q4_ERR_BLOCK = 3,    /* K not a multiple of the block size, or block size invalid for the format */
-    Q4_ERR_FORMAT = 4,   /* unknown format or dtype, or bits != 4 */
+    Q4_ERR_FORMAT = 4,   /* unknown format or dtype, or a code width the entry point does not decode */
     Q4_ERR_ALIGN = 5,    /* a pointer is not aligned as its argument requires */
     Q4_ERR_HIP = 6,      /* a kernel launch failed */
     Q4_ERR_RANGE = 7     /* row range [m0, m1) outside [0, M] or empty */
@@ -128,7 +138,9 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
  * Prefill GEMM, any M >= 1: Y[m][n] as q4_gemv for every row m, computed on
  * the int8 matrix cores (int32 accumulation within a block or group, float
  * rescale per block). Same arguments as q4_gemv with xq [M][K], xs, xsum
- * [M][K/bs], y [M][N]. M*K and N*K/2 must be below 2^31.
+ * [M][K/bs], y [M][N]; affine codes may be 4, 6 or 8 bits (bits; 8-bit codes
+ * enter the matrix cores as q - 128 with 128*s folded into the bias term).
+ * M*K and N*K*bits/8 must be below 2^31.
  * Two kernels, chosen by M:
  *   M <= 32: every weight block is read once for all rows (16x16x32 int8
  *     MFMA, 16 output columns per workgroup, K chunks staged in LDS and split
@@ -177,8 +189,9 @@ int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y,
  *   Q4_0 (bs 32):  i = first index of the largest |w| in the block,
  *                  d = fp16(w[i] / -8), q = clamp(round_half_even(w / d) + 8, 0, 15)
  *                  (q = 8 when d == 0);
- *   affine (bs g): s = bf16((max - min) / 15), b = bf16(min),
- *                  q = clamp(round_half_even((w - b) / s), 0, 15) (q = 0 when s == 0);
+ *   affine (bs g): s = bf16((max - min) / (2^bits - 1)), b = bf16(min),
+ *                  q = clamp(round_half_even((w - b) / s), 0, 2^bits - 1) (q = 0 when s == 0),
+ *                  bits 4, 6 or 8 (codes in the layout above);
  *   every step in float32. wq as above (16-byte aligned); wscale, wbias as in
  *   the format enum (wbias unused for Q4_0).
  * q4k_quantize_weights: w [N][K] float32 -> Q4_K blocks. For each 32-weight
