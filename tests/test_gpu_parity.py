@@ -634,9 +634,13 @@ def test_q4k_ragged(M, K, N):
 
 def test_bit_width_guard_on_device():
     print("case bit-width guard", flush=True)
+    # Q4_0 is 4-bit only: with a code array sized for 8-bit codes the binding passes the
+    # call through and the library's own width guard must reject it
     wts, act = _partials_case("q4_0", 32, 1, 64, 4, 1)
+    wq, wd, wb = _wts_dev("q4_0", wts)
+    wq8 = torch.zeros(q4.code_shape(4, 64, 8), dtype=torch.uint8, device=wq.device)
     with pytest.raises(q4.Q4Error) as e:
-        q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act], bits=8)
+        q4.gemm("q4_0", 32, wq8, wd, wb, *[to_dev(a) for a in act], bits=8)
     assert e.value.status == 4
 
 
