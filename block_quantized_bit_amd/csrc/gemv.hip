@@ -10,14 +10,20 @@
 // Mapping: a workgroup of W wavefronts owns W*R consecutive weight rows; each
 // wavefront owns R rows. A row is K/32 chunks of 16 bytes (32 codes); lane l
 // takes chunks l, l + 64, ... of each of its rows, so every load instruction
-// of a wavefront reads 1 KiB of contiguous codes with 128-bit loads. All code
-// and scale loads of a pass are issued before any arithmetic.
-// While they are in flight the fused variant quantizes x into LDS (4 elements
-// per thread, the lanes of one block combine maxima and sums by lane
-// exchange); a large workgroup (16 wavefronts by default) shares that work.
-// The plain variant reads each chunk's codes straight from global memory (or,
-// as a tuning option, copies them to LDS first). Each lane reads its chunk's
-// 32 codes once and reuses them for all R rows.
+// of a wavefront reads 1 KiB of contiguous codes with 128-bit loads.
+// Every load is a buffer load with no branch around it: a wavefront's buffer
+// range covers only its own rows, and an offset past the end reads zero, so
+// rows past N and chunks past K need no bounds branches (a branch around a
+// load makes the compiler wait for it at the branch's end, which serialised
+// the passes). Scales stay raw 16-bit values until they are used.
+// Order of a launch: the fused variant first issues the loads of its
+// activations, then the first pass of code and scale loads, and quantizes x
+// into LDS while those are in flight (block maxima and sums combine over 8 or
+// 16 lanes with DPP row operations); a large workgroup (16 wavefronts) shares
+// that work. Each pass then prefetches the next pass's loads before its own
+// arithmetic. The plain variant reads each chunk's codes straight from global
+// memory (or, as a tuning option, copies them to LDS first). Each lane reads
+// its chunk's 32 codes once and reuses them for all R rows.
 // The two nibble planes of a chunk pair with the two 16-byte halves of the
 // activation block, so the unpack is one AND (low) and one shift + AND (high)
 // per dword with no byte shuffles; eight v_dot4_i32_i8 give the block's
@@ -33,6 +39,14 @@ namespace q4 {
 
 namespace {
 
+constexpr int RSRC_WORD3 = 0x00020000;
+constexpr uint32_t OUT = 0x80000000u;  // beyond every buffer range: reads as zero
+constexpr int W_AUX = 2;               // non-temporal weight loads: each weight byte is read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
+}
+
 __device__ __forceinline__ int dot_chunk(const uint4& w, const uint4& xa, const uint4& xb) {
     int d = 0;
     d = __builtin_amdgcn_sdot4((int)lo_nibbles(w.x), (int)xa.x, d, false);
@@ -47,71 +61,137 @@ __device__ __forceinline__ int dot_chunk(const uint4& w, const uint4& xa, const 
 }
 
 constexpr int U = 2;  // chunks per lane per pass (a pass covers 64*U chunks = 4096 weights)
-constexpr int EPT = 4;  // activations per thread while staging
 
-// Stage the activation codes of the whole row in LDS.
-// FUSED: quantize x (float32 or bfloat16) per block of G, EPT elements per
-// thread, the G/EPT lanes of a block combining maxima and sums by lane
-// exchange; else copy xq / xs / xsum.
-template <int G, int NT, bool FUSED, bool XBF16>
-__device__ __forceinline__ void stage_activations(int K, const void* __restrict__ x, const int8_t* __restrict__ xq,
-                                                  const float* __restrict__ xs, const int32_t* __restrict__ xsum,
-                                                  int8_t* xq_l, float* xs_l, int32_t* xsum_l, int8_t* xq_out,
-                                                  float* xs_out, int32_t* xsum_out) {
-    const int tid = threadIdx.x;
-    const int ngroups = K / G;
-    if (FUSED) {
-        constexpr int L = G / EPT;  // lanes per block
-        const bool out = xq_out != nullptr && blockIdx.x == 0;
-        for (int u = tid; u < K / EPT; u += NT) {
-            float v[EPT];
-            if (XBF16) {
-                const uint2 p = reinterpret_cast<const uint2*>(x)[u];
-                v[0] = bf16_to_float(p.x & 0xFFFFu);
-                v[1] = bf16_to_float(p.x >> 16);
-                v[2] = bf16_to_float(p.y & 0xFFFFu);
-                v[3] = bf16_to_float(p.y >> 16);
-            } else {
-                const float4 a = reinterpret_cast<const float4*>(x)[u];
-                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            }
-            float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+// Activations per thread while quantizing: the G / EPT lanes of a block then
+// span 8 or 16 lanes, inside one DPP row.
+template <int G>
+constexpr int ept() { return G == 128 ? 8 : 4; }
+constexpr int XPRE = 16;  // activations per thread loaded ahead of the weights
+
+// Maximum / sum over aligned groups of L lanes (L = 8 or 16) by DPP: two quad
+// permutes, a half-row mirror and, for 16, a row mirror. Every lane of the
+// group receives the result.
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    if (L == 16)
+        v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+template <int L>
+__device__ __forceinline__ int group_sum(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    if (L == 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
+    return v;
+}
+
+// EPT consecutive activations of item u (elements EPT*u ...), float32 or
+// bfloat16; an item beyond the row reads as zeros.
+template <int EPT, bool XBF16>
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t r_x, int u, bool in, float (&v)[EPT]) {
+    if (XBF16) {
+        uint32_t p[EPT / 2];
+        if (EPT == 4) {
+            const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r_x, in ? 8u * u : OUT, 0, 0));
+            p[0] = t.x; p[1] = t.y;
+        } else {
+            const uint4 t = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? 16u * u : OUT, 0, 0));
+            p[0] = t.x; p[1] = t.y; p[2 % (EPT / 2)] = t.z; p[3 % (EPT / 2)] = t.w;
+        }
 #pragma unroll
-            for (int off = 1; off < L; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-            const float s = amax / 127.0f;
-            const float inv = act_inverse(s);
-            uint32_t pk = 0;
-            int sum = 0;
-#pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const int c = (amax != 0.0f) ? act_code(v[i], s, inv) : 0;
-                sum += c;
-                pk |= (uint32_t)(c & 0xFF) << (8 * i);
-            }
-#pragma unroll
-            for (int off = 1; off < L; off <<= 1) sum += __shfl_xor(sum, off, 64);
-            reinterpret_cast<uint32_t*>(xq_l)[u] = pk;
-            if (out) reinterpret_cast<uint32_t*>(xq_out)[u] = pk;
-            if ((u & (L - 1)) == 0) {
-                const int g = u / L;
-                const float sv = (amax != 0.0f) ? s : 0.0f;
-                xs_l[g] = sv;
-                xsum_l[g] = sum;
-                if (out) {
-                    xs_out[g] = sv;
-                    xsum_out[g] = sum;
-                }
-            }
+        for (int i = 0; i < EPT / 2; ++i) {
+            v[2 * i] = bf16_to_float(p[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_to_float(p[i] >> 16);
         }
     } else {
-        for (int u = tid; u < (K >> 4); u += NT)
-            reinterpret_cast<uint4*>(xq_l)[u] = reinterpret_cast<const uint4*>(xq)[u];
-        for (int g = tid; g < ngroups; g += NT) {
-            if (xs) xs_l[g] = xs[g];
-            xsum_l[g] = xsum[g];
+#pragma unroll
+        for (int h = 0; h < EPT / 4; ++h) {
+            const float4 t = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            r_x, in ? 4u * (EPT * u + 4 * h) : OUT, 0, 0));
+            v[4 * h] = t.x; v[4 * h + 1] = t.y; v[4 * h + 2] = t.z; v[4 * h + 3] = t.w;
         }
     }
 }
+
+// Quantize item u: all lanes take part (the exchanges need every lane of a
+// block); the stores are made only for items inside the row.
+template <int G, int EPT>
+__device__ __forceinline__ void quantize_item(int u, bool in, const float (&v)[EPT], bool out, int8_t* xq_l,
+                                              float* xs_l, int32_t* xsum_l, int8_t* xq_out, float* xs_out,
+                                              int32_t* xsum_out) {
+    constexpr int L = G / EPT;  // lanes per block
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = group_max<L>(amax);
+    const float s = amax / 127.0f;
+    const float inv = act_inverse(s);
+    uint32_t pk[EPT / 4];
+    int sum = 0;
+#pragma unroll
+    for (int h = 0; h < EPT / 4; ++h) {
+        pk[h] = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = (amax != 0.0f) ? act_code(v[4 * h + i], s, inv) : 0;
+            sum += c;
+            pk[h] |= (uint32_t)(c & 0xFF) << (8 * i);
+        }
+    }
+    sum = group_sum<L>(sum);
+    if (in) {
+        if (EPT == 4) {
+            reinterpret_cast<uint32_t*>(xq_l)[u] = pk[0];
+            if (out) reinterpret_cast<uint32_t*>(xq_out)[u] = pk[0];
+        } else {
+            reinterpret_cast<uint2*>(xq_l)[u] = make_uint2(pk[0], pk[(EPT / 4) - 1]);
+            if (out) reinterpret_cast<uint2*>(xq_out)[u] = make_uint2(pk[0], pk[(EPT / 4) - 1]);
+        }
+        if ((u & (L - 1)) == 0) {
+            const int g = u / L;
+            const float sv = (amax != 0.0f) ? s : 0.0f;
+            xs_l[g] = sv;
+            xsum_l[g] = sum;
+            if (out) {
+                xs_out[g] = sv;
+                xsum_out[g] = sum;
+            }
+        }
+    }
+}
+
+// One pass of weight loads: lane l takes chunks c0 + l + 64 u of each of its
+// R rows (16 bytes of codes each) and the raw 16-bit scale (and bias) of the
+// chunk's block. Out-of-range chunks and rows read as zero.
+template <int FMT, int G, int R, bool PARTIALS>
+struct Pass {
+    uint4 w[R][U];
+    uint32_t s[R][U], b[R][U];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_s,
+                                         __amdgpu_buffer_rsrc_t r_b, int c0, int lane, int nchunks, int ngroups,
+                                         uint32_t rowbytes) {
+        constexpr int CPG = G / 32;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + lane + 64 * u;
+                const bool in = c < nchunks;
+                w[r][u] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, in ? r * rowbytes + 16u * c : OUT, 0, W_AUX));
+                if (!PARTIALS) {
+                    const uint32_t so = in ? 2u * (r * ngroups + c / CPG) : OUT;
+                    s[r][u] = __builtin_amdgcn_raw_buffer_load_b16(r_s, so, 0, 0);
+                    if (FMT == 1) b[r][u] = __builtin_amdgcn_raw_buffer_load_b16(r_b, so, 0, 0);
+                }
+            }
+    }
+};
 
 // FMT 0: Q4_0 (G = 32, fp16 scale, value d * (q - 8)); FMT 1: affine (G = 64
 // or 128, bf16 scale s and bias b, value s * q + b). WAVES wavefronts per
@@ -125,73 +205,100 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     int32_t* __restrict__ partials, int8_t* __restrict__ xq_out, float* __restrict__ xs_out,
     int32_t* __restrict__ xsum_out) {
     constexpr int CPG = G / 32;  // chunks per block / group
+    constexpr int NT = 64 * WAVES;
+    constexpr int EPT = ept<G>();
+    constexpr int NPRE = XPRE / EPT;  // items per thread loaded ahead
     extern __shared__ __attribute__((aligned(16))) int8_t lds[];
     int8_t* xq_l = lds;                                           // K bytes
     float* xs_l = reinterpret_cast<float*>(lds + K);             // K/G floats
     int32_t* xsum_l = reinterpret_cast<int32_t*>(xs_l + K / G);  // K/G ints
 
-    const int lane = threadIdx.x & 63;
-    const int row0 = (blockIdx.x * WAVES + (threadIdx.x >> 6)) * R;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row0 = (blockIdx.x * WAVES + wave) * R;
+    const int nrows = max(0, min(R, N - row0));
     const int nchunks = K >> 5;
     const int ngroups = K / G;
-    const size_t rowbytes = (size_t)(K >> 1);
+    const uint32_t rowbytes = (uint32_t)(K >> 1);
+
+    // the wave's own rows: a range of nrows rows, so that rows past N read zero
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(wq + (size_t)row0 * rowbytes, nrows * rowbytes);
+    const __amdgpu_buffer_rsrc_t r_s = rsrc(wscale + (size_t)row0 * ngroups, PARTIALS ? 0u : nrows * ngroups * 2u);
+    const __amdgpu_buffer_rsrc_t r_b =
+        rsrc(wbias + (size_t)row0 * ngroups, (PARTIALS || FMT == 0) ? 0u : nrows * ngroups * 2u);
+
+    // fused: the activations go out first, so that their quantization below
+    // overlaps the weight stream
+    const int nitems = K / EPT;
+    float xv[NPRE][EPT];
+    const __amdgpu_buffer_rsrc_t r_x = rsrc(x, FUSED ? (uint32_t)K * (XBF16 ? 2u : 4u) : 0u);
+    if (FUSED) {
+#pragma unroll
+        for (int i = 0; i < NPRE; ++i) {
+            const int u = tid + i * NT;
+            if (i * NT < nitems) load_x<EPT, XBF16>(r_x, u, u < nitems, xv[i]);
+        }
+    }
+
+    Pass<FMT, G, R, PARTIALS> cur;
+    cur.load(r_w, r_s, r_b, 0, lane, nchunks, ngroups, rowbytes);
+
+    if (LDS_ACT) {
+        if (FUSED) {
+            const bool out = xq_out != nullptr && blockIdx.x == 0;
+#pragma unroll
+            for (int i = 0; i < NPRE; ++i) {
+                const int u = tid + i * NT;
+                if (i * NT + wave * 64 < nitems)
+                    quantize_item<G, EPT>(u, u < nitems, xv[i], out, xq_l, xs_l, xsum_l, xq_out, xs_out, xsum_out);
+            }
+            for (int ub = NPRE * NT + wave * 64; ub < nitems; ub += NT) {
+                const int u = ub + lane;
+                float v[EPT];
+                load_x<EPT, XBF16>(r_x, u, u < nitems, v);
+                quantize_item<G, EPT>(u, u < nitems, v, out, xq_l, xs_l, xsum_l, xq_out, xs_out, xsum_out);
+            }
+        } else {
+            for (int u = tid; u < (K >> 4); u += NT)
+                reinterpret_cast<uint4*>(xq_l)[u] = reinterpret_cast<const uint4*>(xq)[u];
+            for (int g = tid; g < ngroups; g += NT) {
+                if (xs) xs_l[g] = xs[g];
+                xsum_l[g] = xsum[g];
+            }
+        }
+        __syncthreads();
+    }
 
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0f;
 
     for (int c0 = 0; c0 < nchunks; c0 += 64 * U) {
-        uint4 w[R][U];
-        float sc[R][U], sb[R][U];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int n = row0 + r, c = c0 + lane + 64 * u;
-                sc[r][u] = sb[r][u] = 0.0f;
-                if (n < N && c < nchunks) {
-                    w[r][u] = *reinterpret_cast<const uint4*>(wq + (size_t)n * rowbytes + 16 * (size_t)c);
-                    if (!PARTIALS) {
-                        const size_t si = (size_t)n * ngroups + c / CPG;
-                        if (FMT == 0) {
-                            sc[r][u] = half_to_float(wscale[si]);
-                        } else {
-                            sc[r][u] = bf16_to_float(wscale[si]);
-                            sb[r][u] = bf16_to_float(wbias[si]);
-                        }
-                    }
-                } else {
-                    w[r][u] = make_uint4(0, 0, 0, 0);
-                }
-            }
-        if (LDS_ACT && c0 == 0) {
-            stage_activations<G, 64 * WAVES, FUSED, XBF16>(K, x, xq, xs, xsum, xq_l, xs_l, xsum_l, xq_out, xs_out,
-                                                           xsum_out);
-            __syncthreads();
-        }
+        Pass<FMT, G, R, PARTIALS> nxt;
+        if (c0 + 64 * U < nchunks) nxt.load(r_w, r_s, r_b, c0 + 64 * U, lane, nchunks, ngroups, rowbytes);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = c0 + lane + 64 * u;
-            const bool valid = c < nchunks;
-            uint4 xa = make_uint4(0, 0, 0, 0), xb = xa;
+            const int cc = min(c, nchunks - 1);  // a chunk past the row has zero codes and scales
+            const int gi = cc / CPG;
+            uint4 xa, xb;
             float a = 0.0f;
-            int s = 0;
-            if (valid) {
-                if (LDS_ACT) {
-                    xa = *reinterpret_cast<const uint4*>(xq_l + 32 * c);
-                    xb = *reinterpret_cast<const uint4*>(xq_l + 32 * c + 16);
-                    if (!PARTIALS) a = xs_l[c / CPG];
-                    s = xsum_l[c / CPG];
-                } else {
-                    xa = *reinterpret_cast<const uint4*>(xq + 32 * c);
-                    xb = *reinterpret_cast<const uint4*>(xq + 32 * c + 16);
-                    if (!PARTIALS) a = xs[c / CPG];
-                    s = xsum[c / CPG];
-                }
+            int s;
+            if (LDS_ACT) {
+                xa = *reinterpret_cast<const uint4*>(xq_l + 32 * cc);
+                xb = *reinterpret_cast<const uint4*>(xq_l + 32 * cc + 16);
+                if (!PARTIALS) a = xs_l[gi];
+                s = xsum_l[gi];
+            } else {
+                xa = *reinterpret_cast<const uint4*>(xq + 32 * cc);
+                xb = *reinterpret_cast<const uint4*>(xq + 32 * cc + 16);
+                if (!PARTIALS) a = xs[gi];
+                s = xsum[gi];
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int dot = dot_chunk(w[r][u], xa, xb);
+                const int dot = dot_chunk(cur.w[r][u], xa, xb);
                 if (PARTIALS) {
                     int p = dot;
                     if (FMT == 0) {
@@ -200,23 +307,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
 #pragma unroll
                         for (int off = 1; off < CPG; off <<= 1) p += __shfl_xor(p, off, 64);
                     }
-                    const int n = row0 + r;
-                    if (valid && n < N && (c % CPG) == 0) partials[(size_t)n * ngroups + c / CPG] = p;
+                    if (c < nchunks && r < nrows && (c % CPG) == 0)
+                        partials[(size_t)(row0 + r) * ngroups + c / CPG] = p;
                 } else if (FMT == 0) {
                     const int p = dot - 8 * s;  // sum (q - 8) * xq over the block
-                    acc[r] += (sc[r][u] * a) * (float)p;
+                    acc[r] += (half_to_float(cur.s[r][u]) * a) * (float)p;
                 } else {
-                    acc[r] += a * (sc[r][u] * (float)dot);
-                    if ((c % CPG) == 0) acc[r] += a * (sb[r][u] * (float)s);  // bias * dequantized sum x
+                    acc[r] += a * (bf16_to_float(cur.s[r][u]) * (float)dot);
+                    const float bt = a * (bf16_to_float(cur.b[r][u]) * (float)s);  // bias * dequantized sum x
+                    acc[r] += ((c % CPG) == 0) ? bt : 0.0f;
                 }
             }
         }
+        cur = nxt;
     }
     if (!PARTIALS) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float t = wave_sum(acc[r]);
-            if (lane == 0 && row0 + r < N) y[row0 + r] = t;
+            if (lane == 0 && r < nrows) y[row0 + r] = t;
         }
     }
 }
