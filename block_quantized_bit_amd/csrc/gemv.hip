@@ -132,12 +132,26 @@ __device__ __forceinline__ void quantize_item(int u, bool in, const float (&v)[E
     const float inv = act_inverse(s);
     uint32_t pk[EPT / 4];
     int sum = 0;
+    // act_code for the EPT values: quotients by the reciprocal, then one branch
+    // (rarely taken) to the exact quotients of values near a rounding tie
+    float rq[EPT];
+    bool near = inv == 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        rq[i] = v[i] * inv;
+        near |= fabsf((rq[i] - floorf(rq[i])) - 0.5f) < 0x1p-12f;
+    }
+    if (near) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i)
+            if (inv == 0.0f || fabsf((rq[i] - floorf(rq[i])) - 0.5f) < 0x1p-12f) rq[i] = v[i] / s;
+    }
 #pragma unroll
     for (int h = 0; h < EPT / 4; ++h) {
         pk[h] = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = (amax != 0.0f) ? act_code(v[4 * h + i], s, inv) : 0;
+            const int c = (amax != 0.0f) ? min(127, max(-127, (int)rintf(rq[4 * h + i]))) : 0;
             sum += c;
             pk[h] |= (uint32_t)(c & 0xFF) << (8 * i);
         }
@@ -170,7 +184,7 @@ __device__ __forceinline__ void quantize_item(int u, bool in, const float (&v)[E
 template <int FMT, int G, int R, bool PARTIALS>
 struct Pass {
     uint4 w[R][U];
-    uint32_t s[R][U], b[R][U];
+    uint16_t s[R][U], b[R][U];  // raw fp16 / bf16 bits, converted where used
 
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_s,
                                          __amdgpu_buffer_rsrc_t r_b, int c0, int lane, int nchunks, int ngroups,
