@@ -37,6 +37,20 @@ __device__ __forceinline__ void q4k_pair_scales(const uint4& hdr, int c, float& 
 
 __device__ __forceinline__ float byte_f(uint32_t v, int b) { return (float)((v >> (8 * b)) & 0xFFu); }
 
+// Nibbles isolated into bytes, with the known-zero high bits of each byte
+// hidden from the compiler: it then converts byte b with v_cvt_f32_ubyte<b>
+// rather than a bit-field extract followed by a conversion.
+__device__ __forceinline__ uint32_t nibbles_lo(uint32_t w) {
+    uint32_t v = lo_nibbles(w);
+    __asm__("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t nibbles_hi(uint32_t w) {
+    uint32_t v = hi_nibbles(w);
+    __asm__("" : "+v"(v));
+    return v;
+}
+
 // Sum over 16 weights of code * x for the 4 dwords `q` (nibbles already
 // isolated into bytes) against 16 activations.
 __device__ __forceinline__ float dot16(const uint32_t q[4], const float* x) {
@@ -48,84 +62,105 @@ __device__ __forceinline__ float dot16(const uint32_t q[4], const float* x) {
     return a;
 }
 
-// GEMV: wavefronts walk rows (R rows per pass, loads of all R rows issued
-// before any arithmetic). Lane l owns qs chunks u = l + 64 i of every row; the
-// activations of its chunks (and their sums per half) are loaded once and stay
-// in registers. UPL = chunks per lane (K / 2048, rounded up).
+constexpr int RSRC_WORD3 = 0x00020000;
+constexpr uint32_t OUT = 0x80000000u;  // beyond every buffer range: reads as zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
+}
+
+// One pass of the GEMV: header and qs chunk of each of the lane's UPL chunks,
+// for R consecutive rows of the wavefront.
 template <int UPL, int R>
-__global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, const uint8_t* __restrict__ blocks,
+struct Q4kPass {
+    uint4 hdr[R][UPL], qs[R][UPL];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r_w, int row, int lane, int units, uint32_t rowbytes,
+                                         int j) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) {
+                const int u = lane + 64 * i;
+                const uint32_t o = u < units ? (uint32_t)(row + r) * rowbytes + (uint32_t)(u >> 3) * BLOCK_BYTES : OUT;
+                hdr[r][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
+                qs[r][i] = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 16 + 16 * j, 0, 0));
+            }
+    }
+};
+
+// GEMV: each wavefront owns a contiguous range of rows and walks it R rows per
+// pass, prefetching the next pass before the arithmetic of the current one.
+// Lane l owns qs chunks u = l + 64 i of every row; the activations of its
+// chunks (and their sums per half) are loaded once and stay in registers.
+// Every load is a buffer load with no branch around it: the wavefront's buffer
+// range covers only its own rows, and offsets past the end read zero (a zero
+// header makes a row's terms zero). UPL = chunks per lane (K / 2048, rounded up).
+template <int UPL, int R>
+__global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, int rows_per_wave,
+                                                       const uint8_t* __restrict__ blocks,
                                                        const float* __restrict__ x, float* __restrict__ y) {
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nwaves = gridDim.x * 4;
+    const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = gw * rows_per_wave;
+    const int nrows = max(0, min(rows_per_wave, N - row0));
+    if (nrows == 0) return;
     const int units = K >> 5;
-    const int nsb = K >> 8;
+    const uint32_t rowbytes = (uint32_t)(K >> 8) * BLOCK_BYTES;
     const int j = lane & 7;  // qs chunk within a block (u % 8 == lane % 8)
     const int c = j >> 1, l0 = 16 * (j & 1);
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(blocks + (size_t)row0 * rowbytes, (uint32_t)nrows * rowbytes);
+    const __amdgpu_buffer_rsrc_t r_x = rsrc(x, (uint32_t)K * 4u);
+
+    Q4kPass<UPL, R> cur;
+    cur.load(r_w, 0, lane, units, rowbytes, j);
 
     float xl[UPL][16], xh[UPL][16], sl[UPL], sh[UPL];
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
         const int u = lane + 64 * i;
+        const bool in = u < units;
+        const uint32_t k = (uint32_t)((u >> 3) * QK + 64 * c + l0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? 4 * (k + 4 * t) : OUT, 0, 0));
+            const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? 4 * (k + 32 + 4 * t) : OUT, 0, 0));
+            xl[i][4 * t] = a.x; xl[i][4 * t + 1] = a.y; xl[i][4 * t + 2] = a.z; xl[i][4 * t + 3] = a.w;
+            xh[i][4 * t] = b.x; xh[i][4 * t + 1] = b.y; xh[i][4 * t + 2] = b.z; xh[i][4 * t + 3] = b.w;
+        }
         sl[i] = sh[i] = 0.0f;
-        if (u < units) {
-            const int k = (u >> 3) * QK + 64 * c + l0;
-            const float4* pl = reinterpret_cast<const float4*>(x + k);
-            const float4* ph = reinterpret_cast<const float4*>(x + k + 32);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float4 a = pl[t], b = ph[t];
-                xl[i][4 * t] = a.x; xl[i][4 * t + 1] = a.y; xl[i][4 * t + 2] = a.z; xl[i][4 * t + 3] = a.w;
-                xh[i][4 * t] = b.x; xh[i][4 * t + 1] = b.y; xh[i][4 * t + 2] = b.z; xh[i][4 * t + 3] = b.w;
-            }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                sl[i] += xl[i][t];
-                sh[i] += xh[i][t];
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) xl[i][t] = xh[i][t] = 0.0f;
+        for (int t = 0; t < 16; ++t) {
+            sl[i] += xl[i][t];
+            sh[i] += xh[i][t];
         }
     }
 
-    for (int nb = gw * R; nb < N; nb += nwaves * R) {
-        uint4 hdr[R][UPL], qs[R][UPL];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int i = 0; i < UPL; ++i) {
-                const int n = nb + r, u = lane + 64 * i;
-                if (n < N && u < units) {
-                    const uint8_t* blk = blocks + ((size_t)n * nsb + (u >> 3)) * BLOCK_BYTES;
-                    hdr[r][i] = *reinterpret_cast<const uint4*>(blk);
-                    qs[r][i] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * j);
-                } else {
-                    hdr[r][i] = make_uint4(0, 0, 0, 0);
-                    qs[r][i] = hdr[r][i];
-                }
-            }
+    for (int p = 0; p < nrows; p += R) {
+        Q4kPass<UPL, R> nxt;
+        if (p + R < nrows) nxt.load(r_w, p + R, lane, units, rowbytes, j);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < UPL; ++i) {
-                const float d = half_to_float(hdr[r][i].x & 0xFFFFu);
-                const float dmin = half_to_float(hdr[r][i].x >> 16);
+                const uint4 h = cur.hdr[r][i], q = cur.qs[r][i];
+                const float d = half_to_float(h.x & 0xFFFFu);
+                const float dmin = half_to_float(h.x >> 16);
                 float sc0, sc1, mm0, mm1;
-                q4k_pair_scales(hdr[r][i], c, sc0, sc1, mm0, mm1);
-                const uint32_t ql[4] = {lo_nibbles(qs[r][i].x), lo_nibbles(qs[r][i].y), lo_nibbles(qs[r][i].z),
-                                        lo_nibbles(qs[r][i].w)};
-                const uint32_t qh[4] = {hi_nibbles(qs[r][i].x), hi_nibbles(qs[r][i].y), hi_nibbles(qs[r][i].z),
-                                        hi_nibbles(qs[r][i].w)};
+                q4k_pair_scales(h, c, sc0, sc1, mm0, mm1);
+                const uint32_t ql[4] = {nibbles_lo(q.x), nibbles_lo(q.y), nibbles_lo(q.z), nibbles_lo(q.w)};
+                const uint32_t qh[4] = {nibbles_hi(q.x), nibbles_hi(q.y), nibbles_hi(q.z), nibbles_hi(q.w)};
                 const float al = dot16(ql, xl[i]);
                 const float ah = dot16(qh, xh[i]);
                 acc += (d * sc0) * al - (dmin * mm0) * sl[i];
                 acc += (d * sc1) * ah - (dmin * mm1) * sh[i];
             }
             acc = wave_sum(acc);
-            if (lane == 0 && nb + r < N) y[nb + r] = acc;
+            if (lane == 0 && p + r < nrows) y[row0 + p + r] = acc;
         }
+        cur = nxt;
     }
 }
 
@@ -155,8 +190,8 @@ __global__ __launch_bounds__(256) void q4k_gemv_long_kernel(int K, int N, const 
         const float d = half_to_float(hdr.x & 0xFFFFu), dmin = half_to_float(hdr.x >> 16);
         float sc0, sc1, mm0, mm1;
         q4k_pair_scales(hdr, c, sc0, sc1, mm0, mm1);
-        const uint32_t ql[4] = {lo_nibbles(q.x), lo_nibbles(q.y), lo_nibbles(q.z), lo_nibbles(q.w)};
-        const uint32_t qh[4] = {hi_nibbles(q.x), hi_nibbles(q.y), hi_nibbles(q.z), hi_nibbles(q.w)};
+        const uint32_t ql[4] = {nibbles_lo(q.x), nibbles_lo(q.y), nibbles_lo(q.z), nibbles_lo(q.w)};
+        const uint32_t qh[4] = {nibbles_hi(q.x), nibbles_hi(q.y), nibbles_hi(q.z), nibbles_hi(q.w)};
         acc += (d * sc0) * dot16(ql, xl) - (dmin * mm0) * sl;
         acc += (d * sc1) * dot16(qh, xh) - (dmin * mm1) * sh;
     }
@@ -210,7 +245,7 @@ __global__ __launch_bounds__(256) void q4k_gemm_kernel(int M, int K, int N, cons
 #pragma unroll
         for (int t4 = 0; t4 < 8; ++t4) {  // low nibbles: weights 64h + 0..31
             const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * t4);
-            const uint32_t ql = lo_nibbles(qw[t4]);
+            const uint32_t ql = nibbles_lo(qw[t4]);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, fmaf(ds0, byte_f(ql, 0), -dm0), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, fmaf(ds0, byte_f(ql, 1), -dm0), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, fmaf(ds0, byte_f(ql, 2), -dm0), acc, 0, 0, 0);
@@ -219,7 +254,7 @@ __global__ __launch_bounds__(256) void q4k_gemm_kernel(int M, int K, int N, cons
 #pragma unroll
         for (int t4 = 0; t4 < 8; ++t4) {  // high nibbles: weights 64h + 32..63
             const float4 xv = *reinterpret_cast<const float4*>(xr + 32 + 4 * t4);
-            const uint32_t qh = hi_nibbles(qw[t4]);
+            const uint32_t qh = nibbles_hi(qw[t4]);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, fmaf(ds1, byte_f(qh, 0), -dm1), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, fmaf(ds1, byte_f(qh, 1), -dm1), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, fmaf(ds1, byte_f(qh, 2), -dm1), acc, 0, 0, 0);
@@ -242,14 +277,15 @@ hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, flo
     const uint8_t* b = static_cast<const uint8_t*>(blocks);
     const int units = K >> 5;
     const int upl = (units + 63) / 64;
-    constexpr int R = 4;
-    const int rows_per_pass_blocks = (N + 4 * R - 1) / (4 * R);
-    const unsigned grid = (unsigned)min(rows_per_pass_blocks, 1024);
+    constexpr int R = 2;
+    const int want = 2048;  // workgroups of 4 wavefronts (8 per CU)
+    const int grid = max(1, min(want, (N + 4 * R - 1) / (4 * R)));
+    const int rpw = (N + 4 * grid - 1) / (4 * grid);
     switch (upl) {
-        case 1: hipLaunchKernelGGL((q4k_gemv_kernel<1, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
-        case 2: hipLaunchKernelGGL((q4k_gemv_kernel<2, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
-        case 3: hipLaunchKernelGGL((q4k_gemv_kernel<3, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
-        case 4: hipLaunchKernelGGL((q4k_gemv_kernel<4, R>), dim3(grid), dim3(256), 0, stream, K, N, b, x, y); break;
+        case 1: hipLaunchKernelGGL((q4k_gemv_kernel<1, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
+        case 2: hipLaunchKernelGGL((q4k_gemv_kernel<2, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
+        case 3: hipLaunchKernelGGL((q4k_gemv_kernel<3, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
+        case 4: hipLaunchKernelGGL((q4k_gemv_kernel<4, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
         default:
             hipLaunchKernelGGL(q4k_gemv_long_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, stream, K, N, b, x,
                                y);
