@@ -6,6 +6,10 @@
 // MLX PR #4802: below M = 32 its int8 path is not taken and x is dequantized
 // instead; here the int8 path covers every M.
 //
+// Up to 4 rows with 4-bit codes go to the GEMV-shaped kernel in gemv.hip
+// (activation codes of all rows in registers, 8 v_dot4 per row and block),
+// which is faster there; the kernel below covers the rest.
+//
 // A workgroup owns 16 output columns and all M rows, so every weight block is
 // read once for all rows. K is walked in chunks of 2048: the workgroup copies
 // the chunk's packed codes (16 rows x 1 KB), activation codes (M rows x 2 KB)
@@ -358,6 +362,8 @@ hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, con
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream) {
     if (M < 1 || M > GEMM_SMALL_MAX_M) return hipErrorInvalidValue;
+    if (gemv_rows_fits(M, K, bits))  // up to 4 rows of 4-bit codes: the GEMV-shaped kernel (gemv.hip)
+        return launch_gemv_rows(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
     if (fmt == 0) {
         if (bits != 4) return hipErrorInvalidValue;
         return launch_fmt<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);

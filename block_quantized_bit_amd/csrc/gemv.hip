@@ -344,6 +344,117 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     }
 }
 
+// Few-row variant (1 <= M <= 4 activation rows, 4-bit codes): the GEMV's
+// weight stream and chunk mapping, with each pass's activation codes and
+// scales of all MR rows loaded into registers, so every unpacked weight chunk
+// feeds MR integer dots. A wavefront owns R consecutive weight rows.
+template <int FMT, int G, int MR, int R, bool PARTIALS>
+__global__ __launch_bounds__(256) void gemv_rows_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
+                                                        const uint16_t* __restrict__ wscale,
+                                                        const uint16_t* __restrict__ wbias,
+                                                        const int8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                        const int32_t* __restrict__ xsum, float* __restrict__ y,
+                                                        int32_t* __restrict__ partials) {
+    constexpr int CPG = G / 32;  // chunks per block / group
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * 4 + wave) * R;
+    const int nrows = max(0, min(R, N - row0));
+    if (nrows == 0) return;
+    const int nchunks = K >> 5;
+    const int ngroups = K / G;
+    const uint32_t rowbytes = (uint32_t)(K >> 1);
+
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(wq + (size_t)row0 * rowbytes, nrows * rowbytes);
+    const __amdgpu_buffer_rsrc_t r_s = rsrc(wscale + (size_t)row0 * ngroups, PARTIALS ? 0u : nrows * ngroups * 2u);
+    const __amdgpu_buffer_rsrc_t r_b =
+        rsrc(wbias + (size_t)row0 * ngroups, (PARTIALS || FMT == 0) ? 0u : nrows * ngroups * 2u);
+    const __amdgpu_buffer_rsrc_t r_a = rsrc(xq, (uint32_t)M * (uint32_t)K);
+    const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)M * ngroups * 4u);
+    const __amdgpu_buffer_rsrc_t r_xsum = rsrc(xsum, (uint32_t)M * ngroups * 4u);
+
+    float acc[R][MR];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[r][m] = 0.0f;
+
+    Pass<FMT, G, R, PARTIALS> cur;
+    cur.load(r_w, r_s, r_b, 0, lane, nchunks, ngroups, rowbytes);
+    for (int c0 = 0; c0 < nchunks; c0 += 64 * U) {
+        // this pass's activation codes, scales and code sums; rows past M and
+        // chunks past K read zero
+        uint4 xa[MR][U], xb[MR][U];
+        float a[MR][U];
+        int sx[MR][U];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + lane + 64 * u;
+                const bool in = c < nchunks && m < M;
+                const uint32_t o = in ? (uint32_t)m * (uint32_t)K + 32u * c : OUT;
+                xa[m][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_a, o, 0, 0));
+                xb[m][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_a, in ? o + 16 : OUT, 0, 0));
+                const uint32_t og = in ? 4u * (uint32_t)(m * ngroups + c / CPG) : OUT;
+                a[m][u] = PARTIALS ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, og, 0, 0));
+                sx[m][u] = (int)__builtin_amdgcn_raw_buffer_load_b32(r_xsum, og, 0, 0);
+            }
+        Pass<FMT, G, R, PARTIALS> nxt;
+        if (c0 + 64 * U < nchunks) nxt.load(r_w, r_s, r_b, c0 + 64 * U, lane, nchunks, ngroups, rowbytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + lane + 64 * u;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint4 w = cur.w[r][u];
+                const uint32_t lo[4] = {lo_nibbles(w.x), lo_nibbles(w.y), lo_nibbles(w.z), lo_nibbles(w.w)};
+                const uint32_t hi[4] = {hi_nibbles(w.x), hi_nibbles(w.y), hi_nibbles(w.z), hi_nibbles(w.w)};
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    int dot = 0;
+                    dot = __builtin_amdgcn_sdot4((int)lo[0], (int)xa[m][u].x, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)lo[1], (int)xa[m][u].y, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)lo[2], (int)xa[m][u].z, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)lo[3], (int)xa[m][u].w, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)hi[0], (int)xb[m][u].x, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)hi[1], (int)xb[m][u].y, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)hi[2], (int)xb[m][u].z, dot, false);
+                    dot = __builtin_amdgcn_sdot4((int)hi[3], (int)xb[m][u].w, dot, false);
+                    if (PARTIALS) {
+                        int p = dot;
+                        if (FMT == 0) {
+                            p = dot - 8 * sx[m][u];
+                        } else {
+#pragma unroll
+                            for (int off = 1; off < CPG; off <<= 1) p += __shfl_xor(p, off, 64);
+                        }
+                        if (c < nchunks && r < nrows && m < M && (c % CPG) == 0)
+                            partials[((size_t)m * N + row0 + r) * ngroups + c / CPG] = p;
+                    } else if (FMT == 0) {
+                        const int p = dot - 8 * sx[m][u];  // sum (q - 8) * xq over the block
+                        acc[r][m] += (half_to_float(cur.s[r][u]) * a[m][u]) * (float)p;
+                    } else {
+                        acc[r][m] += a[m][u] * (bf16_to_float(cur.s[r][u]) * (float)dot);
+                        const float bt = a[m][u] * (bf16_to_float(cur.b[r][u]) * (float)sx[m][u]);
+                        acc[r][m] += ((c % CPG) == 0) ? bt : 0.0f;
+                    }
+                }
+            }
+        }
+        cur = nxt;
+    }
+    if (!PARTIALS) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float t = wave_sum(acc[r][m]);
+                if (lane == 0 && r < nrows && m < M) y[(size_t)m * N + row0 + r] = t;
+            }
+    }
+}
+
 // Launch shape: (rows per wave, waves per workgroup, activations in LDS).
 struct GemvShape {
     int r, waves, lds;
@@ -457,6 +568,54 @@ hipError_t launch_gemv_fused(int K, int N, int bs, int fmt, bool xbf16, const vo
         return launch_fused_fmt<1, 64>(K, N, xbf16, x, wq, wscale, wbias, y, xq_out, xs_out, xsum_out, stream);
     if (bs == 128)
         return launch_fused_fmt<1, 128>(K, N, xbf16, x, wq, wscale, wbias, y, xq_out, xs_out, xsum_out, stream);
+    return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int FMT, int G, int MR, bool PARTIALS>
+hipError_t launch_rows_mr(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
+                          const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
+                          hipStream_t stream) {
+    constexpr int R = 2;  // weight rows per wavefront (4 was slower)
+    const dim3 grid((unsigned)((N + 4 * R - 1) / (4 * R))), block(256);
+    hipLaunchKernelGGL((gemv_rows_kernel<FMT, G, MR, R, PARTIALS>), grid, block, 0, stream, M, K, N, wq,
+                       static_cast<const uint16_t*>(wscale), static_cast<const uint16_t*>(wbias), xq, xs, xsum, y,
+                       partials);
+    return hipGetLastError();
+}
+
+template <int FMT, int G, bool PARTIALS>
+hipError_t launch_rows_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
+                           const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
+                           hipStream_t stream) {
+    if (M == 1)
+        return launch_rows_mr<FMT, G, 1, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (M == 2)
+        return launch_rows_mr<FMT, G, 2, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return launch_rows_mr<FMT, G, 4, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+}
+
+template <int FMT, int G>
+hipError_t launch_rows_p(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
+                         const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
+                         hipStream_t stream) {
+    if (partials)
+        return launch_rows_fmt<FMT, G, true>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return launch_rows_fmt<FMT, G, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+}
+
+}  // namespace
+
+bool gemv_rows_fits(int M, int K, int bits) { return bits == 4 && M >= 1 && M <= GEMV_ROWS_MAX_M && K >= 32; }
+
+hipError_t launch_gemv_rows(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                            const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
+                            int32_t* partials, hipStream_t stream) {
+    if (M < 1 || M > GEMV_ROWS_MAX_M) return hipErrorInvalidValue;
+    if (fmt == 0) return launch_rows_p<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bs == 64) return launch_rows_p<1, 64>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (bs == 128) return launch_rows_p<1, 128>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
     return hipErrorInvalidValue;
 }
 

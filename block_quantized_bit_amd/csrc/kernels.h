@@ -38,6 +38,15 @@ hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, con
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream);
 
+// Few-row GEMV (1 <= M <= GEMV_ROWS_MAX_M, 4-bit codes): the decode GEMV's
+// weight stream with the activation codes of all rows in registers. Taken by
+// launch_gemm_small where gemv_rows_fits. Same arguments as launch_gemm.
+constexpr int GEMV_ROWS_MAX_M = 4;
+bool gemv_rows_fits(int M, int K, int bits);
+hipError_t launch_gemv_rows(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                            const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
+                            int32_t* partials, hipStream_t stream);
+
 // Packed weights for the tiled GEMM (layout in include/q4.h, q4_pack_weights).
 size_t packed_code_bytes(int K, int N);
 size_t packed_scale_bytes(int K, int N, int bs);

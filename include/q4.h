@@ -141,11 +141,15 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
  * [M][K/bs], y [M][N]; affine codes may be 4, 6 or 8 bits (bits; 8-bit codes
  * enter the matrix cores as q - 128 with 128*s folded into the bias term).
  * M*K and N*K*bits/8 must be below 2^31.
- * Two kernels, chosen by M:
- *   M <= 32: every weight block is read once for all rows (16x16x32 int8
- *     MFMA, 16 output columns per workgroup, K chunks staged in LDS and split
- *     over its wavefronts). tract PR #2432 measures decode-sized products as
- *     weight streams; MLX PR #4802 leaves its int8 path below M = 32.
+ * Three kernels, chosen by M (and the code width):
+ *   M <= 4 with 4-bit codes: the decode GEMV's weight stream, each weight
+ *     chunk unpacked once and dotted (v_dot4) with the codes of every row,
+ *     which are held in registers.
+ *   other M <= 32: every weight block is read once for all rows (16x16x32
+ *     int8 MFMA, 16 output columns per workgroup, K chunks staged in LDS and
+ *     split over its wavefronts). tract PR #2432 measures decode-sized
+ *     products as weight streams; MLX PR #4802 leaves its int8 path below
+ *     M = 32.
  *   otherwise: 128 x 128 output tiles on 32x32x32 int8 MFMA, one 32-weight
  *     block per K step.
  */
@@ -157,8 +161,8 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
 /*
  * Debug view of the exact integer partials computed inside q4_gemv
  * (path Q4_PATH_GEMV, needs M == 1) or q4_gemm (Q4_PATH_GEMM: the tiled
- * kernel, any row count; Q4_PATH_SMALL: the few-row kernel, m1 - m0 <= 32,
- * else Q4_ERR_RANGE): the same kernels, compiled
+ * kernel, any row count; Q4_PATH_SMALL: the few-row kernels that q4_gemm
+ * takes for m1 - m0 rows, m1 - m0 <= 32, else Q4_ERR_RANGE): the same kernels, compiled
  * with the partials store in place of the float epilogue.
  * partials [(m1-m0)][N][K/bs] int32 for rows m0 <= m < m1:
  *   Q4_0:   sum_{k in b} (q - 8) * xq[m][k]

@@ -292,7 +292,11 @@ def test_gemm_deterministic():
 
 SMALL_CASES = [("q4_0", 32, 2, 416, 37), ("q4_0", 32, 16, 96, 17), ("q4_0", 32, 17, 4096, 33),
                ("q4_0", 32, 32, 8224, 16), ("affine", 64, 5, 320, 31), ("affine", 64, 32, 4096, 48),
-               ("affine", 128, 3, 14336, 21), ("affine", 128, 24, 384, 129)]
+               ("affine", 128, 3, 14336, 21), ("affine", 128, 24, 384, 129),
+               # up to 4 rows of 4-bit codes: the GEMV-shaped kernel (several K passes, pass tails,
+               # ragged N, and N smaller than a workgroup's rows)
+               ("affine", 64, 4, 4160, 45), ("affine", 128, 1, 8320, 19), ("q4_0", 32, 3, 12320, 7),
+               ("affine", 128, 2, 256, 3), ("q4_0", 32, 4, 32, 9)]
 
 
 @pytest.mark.parametrize("fmt,bs,M,K,N", SMALL_CASES)
