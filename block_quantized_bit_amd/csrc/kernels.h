@@ -58,6 +58,9 @@ hipError_t launch_gemm_packed(int M, int K, int N, int bs, int fmt, const uint8_
 
 // Input gradient with frozen weights, dx = dy . dequant(W); fmt 0 Q4_0, 1 affine
 // (bs 64 / 128), 2 Q4_K. K % 256 == 0. work: backward_ranges(M, K, N) * M * K floats.
+// Up to BWD_ROWS_MAX_M rows take the weight-stream kernel, more rows the
+// matrix-core kernel.
+constexpr int BWD_ROWS_MAX_M = 4;
 int backward_ranges(int M, int K, int N);
 hipError_t launch_backward(int M, int K, int N, int fmt, int bs, const uint8_t* w, const void* wscale,
                            const void* wbias, const float* dy, float* dx, float* work, hipStream_t stream);

@@ -530,7 +530,9 @@ def test_gemm_packed_workload_sampled(name):
 
 # ---------------------------------------------------------------- input gradient, frozen weights
 
-BWD_SHAPES = [(1, 256, 1), (3, 512, 70), (16, 1024, 129), (17, 768, 200), (33, 256, 64)]
+BWD_SHAPES = [(1, 256, 1), (3, 512, 70), (16, 1024, 129), (17, 768, 200), (33, 256, 64),
+              # up to 4 rows: the weight-stream kernel, with two K slices (the second partial) and ragged N
+              (2, 2304, 45), (4, 4352, 19), (1, 4096, 300)]
 
 
 @pytest.mark.parametrize("M,K,N", BWD_SHAPES)
