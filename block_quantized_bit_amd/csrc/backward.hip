@@ -368,25 +368,36 @@ __global__ __launch_bounds__(64 * RW) void backward_rows_kernel(int M, int K, in
     }
 }
 
-// dx[m][k] = sum over ranges c of work[c][m][k], in range order. The loads go
-// out 16 at a time (independent of each other) and are added in order, so the
-// sum is the same as one load and add per range.
-__global__ __launch_bounds__(256) void backward_reduce_kernel(long long total, int nranges, const float* __restrict__ work,
-                                                              float* __restrict__ dx) {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
+// dx[m][k] = sum over ranges c of work[c][m][k] in a fixed order: a workgroup
+// of 8 wavefronts takes 64 consecutive outputs; wavefront w sums ranges
+// w, w + 8, w + 16, ... in order (loads issued 16 at a time), and the eight
+// sums are added as ((0 + 1) + (2 + 3)) + ((4 + 5) + (6 + 7)).
+constexpr int RED_W = 8;
+__global__ __launch_bounds__(64 * RED_W) void backward_reduce_kernel(long long total, int nranges,
+                                                                     const float* __restrict__ work,
+                                                                     float* __restrict__ dx) {
+    __shared__ float part[RED_W][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long i = (long long)blockIdx.x * 64 + lane;
+    const bool in = i < total;
     constexpr int U16 = 16;
     float s = 0.0f;
-    int c = 0;
-    for (; c + U16 <= nranges; c += U16) {
+    int c = wave;
+    for (; c + RED_W * (U16 - 1) < nranges; c += RED_W * U16) {
         float v[U16];
 #pragma unroll
-        for (int j = 0; j < U16; ++j) v[j] = work[(size_t)(c + j) * total + i];
+        for (int j = 0; j < U16; ++j) v[j] = in ? work[(size_t)(c + RED_W * j) * total + i] : 0.0f;
 #pragma unroll
         for (int j = 0; j < U16; ++j) s += v[j];
     }
-    for (; c < nranges; ++c) s += work[(size_t)c * total + i];
-    dx[i] = s;
+    for (; c < nranges; c += RED_W) s += in ? work[(size_t)c * total + i] : 0.0f;
+    part[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && in) {
+        const float a = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+        const float b = (part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]);
+        dx[i] = a + b;
+    }
 }
 
 template <int FMTB, int G, int MR>
@@ -398,8 +409,8 @@ hipError_t launch_rows(int M, int K, int N, const uint8_t* w, const void* ws, co
     hipLaunchKernelGGL((backward_rows_kernel<FMTB, G, MR>), grid, dim3(64 * RW), 0, stream, M, K, N, rpw, w,
                        static_cast<const uint16_t*>(ws), static_cast<const uint16_t*>(wb), dy, work);
     const long long total = (long long)M * K;
-    hipLaunchKernelGGL(backward_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, ng,
-                       work, dx);
+    hipLaunchKernelGGL(backward_reduce_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64 * RED_W), 0, stream, total,
+                       ng, work, dx);
     return hipGetLastError();
 }
 
@@ -415,8 +426,8 @@ hipError_t launch_b(int M, int K, int N, const uint8_t* w, const void* ws, const
     hipLaunchKernelGGL((backward_partial_kernel<FMTB, G>), grid, dim3(BT), 0, stream, M, K, N, rows_per, w,
                        static_cast<const uint16_t*>(ws), static_cast<const uint16_t*>(wb), dy, work);
     const long long total = (long long)M * K;
-    hipLaunchKernelGGL(backward_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, total, nr,
-                       work, dx);
+    hipLaunchKernelGGL(backward_reduce_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64 * RED_W), 0, stream, total,
+                       nr, work, dx);
     return hipGetLastError();
 }
 
