@@ -712,6 +712,29 @@ def test_gemv_fused_decode(fmt, bs, xdt):
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("fmt,bs,xdt,K,N", [("q4_0", 32, "f32", 32768, 70), ("affine", 128, "bf16", 32768, 33),
+                                            ("affine", 64, "bf16", 14336, 129), ("q4_0", 32, "bf16", 14336, 5)])
+def test_gemv_fused_long_k(fmt, bs, xdt, K, N):
+    # past 16 activations per thread the quantizer loops over the rest of x; K = 14336 ends
+    # with a partial pass of weight loads, K = 32768 is the largest K the GEMV takes
+    print(f"case gemv_fused long K {fmt} bs={bs} x={xdt} K={K} N={N}", flush=True)
+    rng = np.random.default_rng(K + N)
+    x32 = rng.standard_normal((1, K)).astype(np.float32)
+    x = synth.bf16_bits(x32) if xdt == "bf16" else x32
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    wts = oracle.quantize_q4_0(w) if fmt == "q4_0" else oracle.quantize_affine(synth.bf16_bits(w), bs)
+    act = oracle.quantize_act(x, bs)
+    gx = to_dev(x)
+    out = (torch.empty((1, K), dtype=torch.int8, device=gx.device),
+           torch.empty((1, K // bs), dtype=torch.float32, device=gx.device),
+           torch.empty((1, K // bs), dtype=torch.int32, device=gx.device))
+    y = q4.gemv_fused(fmt, bs, gx, *_wts_dev(fmt, wts), act_out=out)
+    _sync()
+    for a, b in zip(out, act):
+        assert np.array_equal(to_np(a).view(np.uint8), b.view(np.uint8))
+    assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+
+
 def test_gemv_fused_near_ties_and_ragged():
     print("case gemv_fused near ties, ragged N", flush=True)
     x = _near_tie_activations(1, 8192, 32, 5)
