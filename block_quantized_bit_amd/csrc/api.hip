@@ -248,10 +248,16 @@ int q4_gemm_backward(int M, int K, int N, int bs, int fmt, int bits, const uint8
                                           static_cast<hipStream_t>(stream)));
 }
 
+// The Q4_K kernels address blocks and x with 32-bit buffer offsets.
+static bool q4k_offsets_too_large(int M, int K, int N) {
+    return (long long)N * (K / 256) * 144 >= (1LL << 31) || 4LL * M * K >= (1LL << 31);
+}
+
 int q4k_gemv(int M, int K, int N, const void* blocks, const float* x, float* y, void* stream) {
     if (!blocks || !x || !y) return Q4_ERR_NULL;
     if (M != 1 || N <= 0 || K <= 0) return Q4_ERR_DIM;
     if (K % 256 != 0) return Q4_ERR_BLOCK;
+    if (q4k_offsets_too_large(M, K, N)) return Q4_ERR_DIM;
     if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
     return hip_status(q4::launch_q4k_gemv(K, N, blocks, x, y, static_cast<hipStream_t>(stream)));
 }
@@ -260,6 +266,7 @@ int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, 
     if (!blocks || !x || !y) return Q4_ERR_NULL;
     if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 20)) return Q4_ERR_DIM;  // grid rows of 16
     if (K % 256 != 0) return Q4_ERR_BLOCK;
+    if (q4k_offsets_too_large(M, K, N)) return Q4_ERR_DIM;
     if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4)) return Q4_ERR_ALIGN;
     return hip_status(q4::launch_q4k_gemm(M, K, N, blocks, x, y, static_cast<hipStream_t>(stream)));
 }

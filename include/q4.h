@@ -180,7 +180,9 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits,
  * sum_k (d*sc*q - dmin*m) * x per output row; gemm_q4_k_ref is one GEMV per
  * activation row). Dequantized weights live only in registers.
  * blocks [N][K/256] x 144 bytes (16-byte aligned), x [M][K] float32
- * (16-byte aligned), y [M][N] float32. K must be a multiple of 256.
+ * (16-byte aligned), y [M][N] float32. K must be a multiple of 256. The
+ * kernels address blocks and x with 32-bit byte offsets: N*(K/256)*144 and
+ * 4*M*K must be below 2^31 (else Q4_ERR_DIM).
  */
 int q4k_gemv(int M, int K, int N, const void* blocks, const float* x, float* y,
              void* stream);

@@ -190,6 +190,10 @@ def test_q4k_validation():
         assert f(1, 4096, 0, A, A, A, None) == DIM
         assert f(1, 4096, 8, A + 8, A, A, None) == ALIGN
     assert q4.lib().q4k_gemv(2, 4096, 8, A, A, A, None) == DIM
+    # 32-bit buffer offsets: the weight blocks and x must each stay below 2^31 bytes
+    assert q4.lib().q4k_gemv(1, 32768, 460000, A, A, A, None) == DIM      # 460000 * 128 * 144 bytes
+    assert q4.lib().q4k_gemm(16, 32768, 460000, A, A, A, None) == DIM
+    assert q4.lib().q4k_gemm(20000, 32768, 8, A, A, A, None) == DIM       # 4 * M * K bytes of x
 
 
 def test_weight_quantizer_validation():
