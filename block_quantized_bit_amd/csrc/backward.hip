@@ -9,7 +9,8 @@
 // The contraction runs over N, the weight rows. A workgroup owns one 256-wide
 // column of K (one Q4_K super-block, or 8 Q4_0 blocks / 4 or 2 affine groups),
 // one 16-row tile of dY and one range of weight rows. Every weight byte of the
-// column and range is read once. Rows are staged through LDS 64 at a time in a
+// column and range is read once. Rows are staged through LDS 64 at a time
+// (double-buffered; the next 64 rows' loads wait in registers meanwhile) in a
 // common form: the column's 128 code bytes of the row and eight (a, b) pairs,
 // one per 32-weight sub-block, with w = a*q + b:
 //   Q4_K:   a = d * sc[s], b = -dmin * m[s]      (gemv_q4_k_ref: "w = d * q - m")
@@ -79,10 +80,11 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
                                                                  const uint16_t* __restrict__ wscale,
                                                                  const uint16_t* __restrict__ wbias,
                                                                  const float* __restrict__ dy, float* __restrict__ work) {
-    __shared__ BwdLds S;
+    __shared__ BwdLds S[2];  // stage i in S[i & 1]; the next stage's loads wait in registers
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kb = blockIdx.x, nc = blockIdx.y, m0 = blockIdx.z * 16;
     const int nbeg = nc * rows_per, nend = min(N, nbeg + rows_per);
+    const int nst = nend > nbeg ? (nend - nbeg + RC - 1) / RC : 0;  // 64-row stages of the range
     const int ngroups = K / G;
 
     const uint32_t wbytes = FMTB == 2 ? (uint32_t)((size_t)N * (K / 256) * Q4K_BYTES) : (uint32_t)((size_t)N * (K / 2));
@@ -103,80 +105,95 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int r0 = nbeg; r0 < nend; r0 += RC) {
-        // codes: 4 threads x 32 bytes per row
-        {
-            const int r = tid >> 2, part = tid & 3, n = r0 + r;
-            uint32_t o = OUT;
-            if (n < nend) {
-                o = FMTB == 2 ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES + 16 + 32 * part)
-                              : (uint32_t)((size_t)n * (K / 2) + (size_t)kb * 128 + 32 * part);
-            }
-            // Q4_K blocks are 144 bytes: 16-byte aligned offsets (144 = 9 * 16), so 128-bit loads
-            const uint4 v0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
-            const uint4 v1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 16, 0, 0));
-            *reinterpret_cast<uint4*>(&S.codes[r][32 * part]) = v0;
-            *reinterpret_cast<uint4*>(&S.codes[r][32 * part + 16]) = v1;
+    // staging of one 64-row stage: thread (r, part) = (tid / 4, tid % 4) takes 32 code
+    // bytes and two sub-blocks' (a, b) of row r; 4 dY values per thread
+    const int sr = tid >> 2, part = tid & 3, s0 = 2 * part;
+    uint4 rc0, rc1, rh;
+    uint32_t ra0, ra1, rb0, rb1;
+    float rdy[4];
+    auto load = [&](int r0) {  // rows past the range read zero
+        const int n = r0 + sr;
+        const bool in = n < nend;
+        uint32_t o = OUT;
+        if (FMTB == 2) {
+            o = in ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES + 16 + 32 * part) : OUT;
+            rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               r_w, in ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES) : OUT, 0, 0));
+        } else {
+            o = in ? (uint32_t)((size_t)n * (K / 2) + (size_t)kb * 128 + 32 * part) : OUT;
+            const int g0 = (kb * 256 + 32 * s0) / G, g1 = (kb * 256 + 32 * (s0 + 1)) / G;
+            const uint32_t ob = in ? (uint32_t)((size_t)n * ngroups * 2) : OUT;
+            ra0 = __builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g0 * 2, 0);
+            ra1 = __builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g1 * 2, 0);
+            rb0 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g0 * 2, 0) : 0u;
+            rb1 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g1 * 2, 0) : 0u;
         }
-        // coefficients: 4 threads x 2 sub-blocks per row
-        {
-            const int r = tid >> 2, s0 = 2 * (tid & 3), n = r0 + r;
-            const bool in = n < nend;
-            float2 c0 = make_float2(0.0f, 0.0f), c1 = make_float2(0.0f, 0.0f);
-            if (FMTB == 2) {
-                const uint32_t o = in ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES) : OUT;
-                const uint4 h = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
-                const float d = half_to_float(h.x & 0xFFFFu), dmin = half_to_float(h.x >> 16);
-                // the sixteen 6-bit fields of the 96-bit little-endian string in h.y, h.z, h.w
-                const uint64_t lo = ((uint64_t)h.z << 32) | h.y;
-                const uint32_t hi = h.w;
-                auto field = [&](int f) -> uint32_t {
-                    const int bit = 6 * f;
-                    if (bit + 6 <= 64) return (uint32_t)(lo >> bit) & 63u;
-                    if (bit >= 64) return (hi >> (bit - 64)) & 63u;
-                    return (uint32_t)((lo >> bit) | ((uint64_t)hi << (64 - bit))) & 63u;
-                };
-                c0 = make_float2(d * (float)field(s0), -dmin * (float)field(8 + s0));
-                c1 = make_float2(d * (float)field(s0 + 1), -dmin * (float)field(8 + s0 + 1));
-            } else {
-                const int g0 = (kb * 256 + 32 * s0) / G, g1 = (kb * 256 + 32 * (s0 + 1)) / G;
-                const uint32_t ob = in ? (uint32_t)((size_t)n * ngroups * 2) : OUT;
-                const float a0 = (FMTB == 0) ? half_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g0 * 2, 0))
-                                             : bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g0 * 2, 0));
-                const float a1 = (FMTB == 0) ? half_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g1 * 2, 0))
-                                             : bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g1 * 2, 0));
-                if (FMTB == 0) {
-                    c0 = make_float2(a0, -8.0f * a0);
-                    c1 = make_float2(a1, -8.0f * a1);
-                } else {
-                    c0 = make_float2(a0, bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g0 * 2, 0)));
-                    c1 = make_float2(a1, bf16_to_float(__builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g1 * 2, 0)));
-                }
-            }
-            S.coef[r][s0] = c0;
-            S.coef[r][s0 + 1] = c1;
-        }
-        // dY tile: 16 rows x 64 weight rows, 4 values per thread
+        // Q4_K blocks are 144 bytes: 16-byte aligned offsets (144 = 9 * 16), so 128-bit loads
+        rc0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
+        rc1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 16, 0, 0));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = tid + BT * i, m = idx >> 6, r = idx & 63, n = r0 + r;
-            const uint32_t o = (m0 + m < M && n < nend) ? (uint32_t)(((size_t)(m0 + m) * N + n) * 4) : OUT;
-            S.dy[m][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_dy, o, 0, 0));
+            const int idx = tid + BT * i, m = idx >> 6, r = idx & 63, nn = r0 + r;
+            const uint32_t od = (m0 + m < M && nn < nend) ? (uint32_t)(((size_t)(m0 + m) * N + nn) * 4) : OUT;
+            rdy[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_dy, od, 0, 0));
         }
-        __syncthreads();
+    };
+    auto store = [&](BwdLds& T) {
+        *reinterpret_cast<uint4*>(&T.codes[sr][32 * part]) = rc0;
+        *reinterpret_cast<uint4*>(&T.codes[sr][32 * part + 16]) = rc1;
+        float2 c0, c1;
+        if (FMTB == 2) {
+            const float d = half_to_float(rh.x & 0xFFFFu), dmin = half_to_float(rh.x >> 16);
+            // the sixteen 6-bit fields of the 96-bit little-endian string in h.y, h.z, h.w
+            const uint64_t lo = ((uint64_t)rh.z << 32) | rh.y;
+            const uint32_t hi = rh.w;
+            auto field = [&](int f) -> uint32_t {
+                const int bit = 6 * f;
+                if (bit + 6 <= 64) return (uint32_t)(lo >> bit) & 63u;
+                if (bit >= 64) return (hi >> (bit - 64)) & 63u;
+                return (uint32_t)((lo >> bit) | ((uint64_t)hi << (64 - bit))) & 63u;
+            };
+            c0 = make_float2(d * (float)field(s0), -dmin * (float)field(8 + s0));
+            c1 = make_float2(d * (float)field(s0 + 1), -dmin * (float)field(8 + s0 + 1));
+        } else if (FMTB == 0) {
+            const float a0 = half_to_float(ra0), a1 = half_to_float(ra1);
+            c0 = make_float2(a0, -8.0f * a0);
+            c1 = make_float2(a1, -8.0f * a1);
+        } else {
+            c0 = make_float2(bf16_to_float(ra0), bf16_to_float(rb0));
+            c1 = make_float2(bf16_to_float(ra1), bf16_to_float(rb1));
+        }
+        T.coef[sr][s0] = c0;
+        T.coef[sr][s0 + 1] = c1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + BT * i, m = idx >> 6, r = idx & 63;
+            T.dy[m][r] = rdy[i];
+        }
+    };
+
+    if (nst > 0) {
+        load(nbeg);
+        store(S[0]);
+        load(nbeg + RC);
+    }
+    for (int i = 0; i < nst; ++i) {
+        __syncthreads();  // stage i is in S[i & 1]; every wavefront is done with S[(i + 1) & 1]
+        if (i + 1 < nst) store(S[(i + 1) & 1]);
+        load(nbeg + (i + 2) * RC);
+        const BwdLds& T = S[i & 1];
 #pragma unroll 4
         for (int st = 0; st < RC / 4; ++st) {
             const int rl = 4 * st + (lane >> 4);  // this lane's weight row in the stage
-            const float aop = S.dy[lane & 15][rl];
+            const float aop = T.dy[lane & 15][rl];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int q = (S.codes[rl][bidx[j]] >> bsh[j]) & 15;
-                const float2 c = S.coef[rl][bsub[j]];
+                const int q = (T.codes[rl][bidx[j]] >> bsh[j]) & 15;
+                const float2 c = T.coef[rl][bsub[j]];
                 const float wv = c.x * (float)q + c.y;
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(aop, wv, acc[j], 0, 0, 0);
             }
         }
-        __syncthreads();
     }
     // D layout: lane holds column lane%16, rows 4*(lane/16) + r
 #pragma unroll
