@@ -240,6 +240,8 @@ def test_gemv_ragged(fmt, bs, K, N):
     ("q4_0", 32, 1, 32, 1), ("q4_0", 32, 3, 96, 33), ("q4_0", 32, 65, 160, 1537), ("q4_0", 32, 257, 416, 130),
     ("affine", 64, 1, 64, 5), ("affine", 64, 129, 320, 255), ("affine", 128, 200, 384, 131),
     ("affine", 128, 64, 4224, 64),
+    # few tiles and at least 8 K stages: K split over two wavefront groups per workgroup
+    ("affine", 64, 33, 2048, 129), ("q4_0", 32, 200, 1024, 100),
 ])
 def test_gemm_ragged(fmt, bs, M, K, N):
     print(f"case gemm {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
@@ -392,7 +394,7 @@ def _bits_case(bits, g, M, K, N, seed):
 
 
 BITS_CASES = [(6, 64, 3, 320, 37), (6, 128, 130, 384, 131), (6, 64, 17, 4096, 65), (8, 64, 2, 192, 33),
-              (8, 128, 129, 512, 257), (8, 64, 32, 4096, 48), (8, 128, 200, 1152, 64)]
+              (8, 128, 129, 512, 257), (8, 64, 32, 4096, 48), (8, 128, 200, 1152, 64), (6, 64, 40, 1024, 70)]
 
 
 @pytest.mark.parametrize("bits,g", [(6, 64), (6, 128), (8, 64), (8, 128)])
