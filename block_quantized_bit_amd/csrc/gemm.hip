@@ -22,9 +22,18 @@
 //
 // Per block (Q4_0) or group (affine, 64 / 128 weights = 2 / 4 MFMA steps) the
 // int32 tile is rescaled into float accumulators:
-//   Q4_0:   acc += xs[m] * (d[n] * P)                 3 VALU ops per output
-//   affine: acc += xs[m] * (s[n] * A)                 3 VALU ops per output
+//   Q4_0:   acc += xs[m] * (d[n] * P)                 2 VALU ops per output
+//   affine: acc += xs[m] * (s[n] * A)                 2 VALU ops per output
 //           acc += sum_g (xs * xsum)[m, g] * b[n, g]  on the f32 matrix core
+// The integer-to-float conversion costs no instruction: each group's MFMA
+// chain starts from the integer 0x4B400000 (the bits of C = 1.5 * 2^23)
+// instead of zero. Every block or group sum P or A lies within +-2^22, so the
+// chain ends on the bits of the float C + P exactly, and one FMA with the
+// exact constant -d * C (d has at most 11 significant bits) gives d * P
+// rounded once, as a conversion and a multiply would. The limit this puts on
+// the weight scales: d * C must stay finite, |d| < 2^104. (8-bit codes stage
+// twice the code bytes per thread and keep the conversion: the 16 registers
+// holding the start value do not fit beside them.)
 // The affine bias term is a rank-(K/g) product, so it runs as
 // v_mfma_f32_32x32x2_f32 with two groups in its two K slots instead of a
 // fourth VALU op per output.
@@ -58,6 +67,8 @@ constexpr int GROUP_M = 8;           // row tiles per tile group
 constexpr int NXCD = 8;
 constexpr int RING = 3;              // scale slots
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data format
+constexpr int CHAIN_BIAS = 0x4B400000;  // bits of the float 1.5 * 2^23
+constexpr float CHAIN_BIAS_F = 12582912.0f;
 
 struct Tiles {
     uint4 a[BM * KS / 16];  // int8 activation codes, swizzled 128-byte rows
@@ -323,10 +334,18 @@ __global__ __launch_bounds__(NT * KSP, KSP == 1 ? 2 : 1) void gemm_kernel(int M,
         return __builtin_bit_cast(v4i, base[swz(row, gi * (G / 16) + 2 * s + half)]);
     };
 
+    // Start value of every MFMA chain: the bits of 1.5 * 2^23, or zero for the
+    // partials and 8-bit codes (the empty asm keeps the 16 registers live
+    // instead of rebuilding them before each chain).
+    constexpr bool BIASED = !PARTIALS && BITS != 8;
+    v16i chain0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) chain0[r] = BIASED ? CHAIN_BIAS : 0;
+    if (BIASED) asm("" : "+v"(chain0));
+
     // MFMA chain of one group for one tile.
     auto mfma_tile = [&](v16i& d, const v4i (&fa)[SPG], const v4i (&fb)[SPG]) {
-        const v16i z = {};
-        d = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fb[0], z, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[0], fb[0], chain0, 0, 0, 0);
 #pragma unroll
         for (int s = 1; s < SPG; ++s) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s], fb[s], d, 0, 0, 0);
     };
@@ -367,8 +386,19 @@ __global__ __launch_bounds__(NT * KSP, KSP == 1 ? 2 : 1) void gemm_kernel(int M,
             return;
         }
         const float w = S.ws[gi][brow + 32 * j];
+        if (!BIASED) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += xsv[r] * (w * (float)d[r]);
+            for (int r = 0; r < 16; ++r) acc[i][j][r] += xsv[r] * (w * (float)d[r]);
+            return;
+        }
+        const float wc = w * -CHAIN_BIAS_F;  // exact
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            // copy the element first: clang's bit_cast of a vector element
+            // subscript reads element 0 whatever the index
+            const int e = d[r];
+            acc[i][j][r] += xsv[r] * fmaf(w, __builtin_bit_cast(float, e), wc);
+        }
     };
 
     // Affine bias of two groups on the f32 matrix core for tile (i, j): lanes
