@@ -151,7 +151,10 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
  *     products as weight streams; MLX PR #4802 leaves its int8 path below
  *     M = 32.
  *   otherwise: 128 x 128 output tiles on 32x32x32 int8 MFMA, one 32-weight
- *     block per K step.
+ *     block per K step. For 4- and 6-bit codes this kernel takes each
+ *     block's integer sum into float through an exponent bias, which needs
+ *     |weight scale| < 2^104 (d * 1.5 * 2^23 must stay finite); larger
+ *     scales give infinities instead of the finite result.
  */
 int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
             const uint8_t* wq, const void* wscale, const void* wbias,
@@ -238,8 +241,8 @@ int q4k_quantize_weights(int N, int K, const float* w, void* blocks, void* strea
  * offset 0, then at offset A = align256(M*K) xs as [K/bs][M] float32
  * (group-major, the transpose of q4_quantize_act's xs), then at offset
  * A + align256(4*M*K/bs) xsum as [K/bs][M] int32. Two launches on stream:
- * the quantizer, then the tiled 32x32x32 int8 MFMA GEMM (for every M).
- * M*K must be below 2^31.
+ * the quantizer, then the tiled 32x32x32 int8 MFMA GEMM (for every M),
+ * with the weight-scale limit stated at q4_gemm. M*K must be below 2^31.
  */
 size_t q4_packed_bytes(int K, int N, int bs, int fmt);
 int q4_pack_weights(int N, int K, int bs, int fmt, int bits, const uint8_t* wq,
