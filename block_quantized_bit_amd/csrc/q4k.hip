@@ -93,7 +93,13 @@ struct Q4kPass {
 // GEMV: each wavefront owns a contiguous range of rows and walks it R rows per
 // pass, prefetching the next pass before the arithmetic of the current one.
 // Lane l owns qs chunks u = l + 64 i of every row; the activations of its
-// chunks (and their sums per half) are loaded once and stay in registers.
+// chunks (and their sums per half) stay in registers. The workgroup reads x
+// from memory once: after the first pass of weight loads is issued, its
+// threads copy x into LDS in lane order -- float4 (i, h, t) of lane l at
+// ((2i + h) * 4 + t) * 64 + l, h = 0 for the low-nibble weights, 1 for the
+// high -- so that each wavefront's register fill is 16-byte reads by
+// consecutive lanes (no bank conflicts), and the vector memory path carries
+// x once per workgroup instead of once per wavefront.
 // Every load is a buffer load with no branch around it: the wavefront's buffer
 // range covers only its own rows, and offsets past the end read zero (a zero
 // header makes a row's terms zero). UPL = chunks per lane (K / 2048, rounded up).
@@ -101,11 +107,11 @@ template <int UPL, int R>
 __global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, int rows_per_wave,
                                                        const uint8_t* __restrict__ blocks,
                                                        const float* __restrict__ x, float* __restrict__ y) {
+    __shared__ float4 xlds[UPL * 8 * 64];
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = gw * rows_per_wave;
     const int nrows = max(0, min(rows_per_wave, N - row0));
-    if (nrows == 0) return;
     const int units = K >> 5;
     const uint32_t rowbytes = (uint32_t)(K >> 8) * BLOCK_BYTES;
     const int j = lane & 7;  // qs chunk within a block (u % 8 == lane % 8)
@@ -113,19 +119,31 @@ __global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, int rows_pe
     const __amdgpu_buffer_rsrc_t r_w = rsrc(blocks + (size_t)row0 * rowbytes, (uint32_t)nrows * rowbytes);
     const __amdgpu_buffer_rsrc_t r_x = rsrc(x, (uint32_t)K * 4u);
 
+    // x loads first (in lane order, units past K read zero), then the first
+    // pass of weights; the LDS stores wait only for the x loads
+    float4 xv[UPL * 2];
+#pragma unroll
+    for (int m = 0; m < UPL * 2; ++m) {
+        const int e = (int)threadIdx.x + 256 * m;  // entry ((2i + h) * 4 + t) * 64 + l
+        const int l = e & 63, t = (e >> 6) & 3, h = (e >> 8) & 1, i = e >> 9;
+        const int u = l + 64 * i, jl = l & 7;
+        const uint32_t k = (uint32_t)((u >> 3) * QK + 64 * (jl >> 1) + 16 * (jl & 1) + 32 * h + 4 * t);
+        xv[m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, u < units ? 4 * k : OUT, 0, 0));
+    }
     Q4kPass<UPL, R> cur;
     cur.load(r_w, 0, lane, units, rowbytes, j);
+#pragma unroll
+    for (int m = 0; m < UPL * 2; ++m) xlds[(int)threadIdx.x + 256 * m] = xv[m];
+    __syncthreads();
+    if (nrows == 0) return;
 
     float xl[UPL][16], xh[UPL][16], sl[UPL], sh[UPL];
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
-        const int u = lane + 64 * i;
-        const bool in = u < units;
-        const uint32_t k = (uint32_t)((u >> 3) * QK + 64 * c + l0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? 4 * (k + 4 * t) : OUT, 0, 0));
-            const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? 4 * (k + 32 + 4 * t) : OUT, 0, 0));
+            const float4 a = xlds[((2 * i) * 4 + t) * 64 + lane];
+            const float4 b = xlds[((2 * i + 1) * 4 + t) * 64 + lane];
             xl[i][4 * t] = a.x; xl[i][4 * t + 1] = a.y; xl[i][4 * t + 2] = a.z; xl[i][4 * t + 3] = a.w;
             xh[i][4 * t] = b.x; xh[i][4 * t + 1] = b.y; xh[i][4 * t + 2] = b.z; xh[i][4 * t + 3] = b.w;
         }
@@ -328,8 +346,12 @@ hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, flo
     const uint8_t* b = static_cast<const uint8_t*>(blocks);
     const int units = K >> 5;
     const int upl = (units + 63) / 64;
-    constexpr int R = 2;
-    const int want = 2048;  // workgroups of 4 wavefronts (8 per CU)
+    // one row per pass (115 registers: 4 wavefronts per SIMD) and 1024
+    // workgroups of 4 wavefronts: at 4096 x 14336 each wavefront walks 4 rows,
+    // the next one's loads in flight (measured 10.9 us against 11.3 us for
+    // 2 rows per pass and 2048 workgroups)
+    constexpr int R = 1;
+    const int want = 1024;
     const int grid = max(1, min(want, (N + 4 * R - 1) / (4 * R)));
     const int rpw = (N + 4 * grid - 1) / (4 * grid);
     switch (upl) {

@@ -619,7 +619,12 @@ def test_q4k_gemm_workload():
     assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
 
 
-@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (1, 768, 70), (1, 12288, 33), (1, 20480, 5), (3, 512, 63),
+# The M = 1 cases cover 1 to 4 chunks per lane (K up to 8192), a partly
+# filled last chunk pass (K = 2304: 72 of 128 lanes), the long-row kernel
+# (K > 8192), and N = 4099, where the GEMV grid leaves some wavefronts with
+# no rows (they still take part in the workgroup's activation staging).
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (1, 768, 70), (1, 2304, 3), (1, 4096, 4099), (1, 6144, 9),
+                                   (1, 8192, 130), (1, 12288, 33), (1, 20480, 5), (3, 512, 63),
                                    (16, 256, 64), (17, 1024, 65), (40, 2048, 130)])
 def test_q4k_ragged(M, K, N):
     print(f"case q4k M={M} K={K} N={N}", flush=True)
