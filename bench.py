@@ -271,17 +271,25 @@ def main():
 
     del copies
 
-    def time_eager(fn, iters, warm=3):
+    def time_graphed(fn, iters, warm=3, reps=3):
+        # iters calls captured in one HIP graph and replayed reps times, so that
+        # the host's launch rate does not enter the per-call time of short kernels
         for _ in range(warm):
             fn()
         torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = event_pair()
         e0.record()
-        for _ in range(iters):
-            fn()
+        for _ in range(reps):
+            g.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / iters
+        return e0.elapsed_time(e1) / 1e3 / (iters * reps)
 
     gemm_cases = [("gemm_3a", "affine_g128_4096x4096x14336", 20), ("gemm_3b", "affine_g128_4096x14336x4096", 20),
                   ("gemm_2", "affine_g64_1024x4096x4096", 50), ("gemm_0", "q4_0_minilm_64x384x1536", 200)]
@@ -301,8 +309,8 @@ def main():
         del wt
         xq, xs, xsum = q4.quantize_act(xt, g.bs)
         yy = torch.empty((g.M, g.N), dtype=torch.float32, device=dev)
-        t_gemm = time_eager(lambda: q4.gemm(g.fmt, g.bs, gwq, gws, gwb, xq, xs, xsum, y=yy), iters)
-        t_act = time_eager(lambda: q4.quantize_act(xt, g.bs, out=(xq, xs, xsum)), iters)
+        t_gemm = time_graphed(lambda: q4.gemm(g.fmt, g.bs, gwq, gws, gwb, xq, xs, xsum, y=yy), iters)
+        t_act = time_graphed(lambda: q4.quantize_act(xt, g.bs, out=(xq, xs, xsum)), iters)
         ops = 2.0 * g.M * g.N * g.K
         act_bytes = xt.numel() * xt.element_size() + xq.numel() + 8 * xs.numel()
         entry = {
@@ -315,7 +323,7 @@ def main():
             packed = q4.pack_weights(g.fmt, g.bs, gwq, gws, gwb)
             work = torch.empty(int(q4.lib().q4_gemm_packed_work_bytes(g.M, g.K, g.bs)), dtype=torch.uint8,
                                device=dev)
-            t_pk = time_eager(lambda: q4.gemm_packed(g.fmt, g.bs, xt, packed, g.N, y=yy, work=work), iters)
+            t_pk = time_graphed(lambda: q4.gemm_packed(g.fmt, g.bs, xt, packed, g.N, y=yy, work=work), iters)
             entry.update({"packed_step_us": round(t_pk * 1e6, 2), "packed_step_TOPS": round(ops / t_pk / 1e12, 1),
                           "packed_gemm_us_est": round((t_pk - t_act) * 1e6, 2),
                           "packed_gemm_frac_int8_peak_est": round(ops / (t_pk - t_act) / 1e12 / INT8_PEAK_TOPS, 4)})
@@ -335,7 +343,7 @@ def main():
             ops = 2.0 * g.M * g.N * g.K
             for bits in (4, 6, 8):
                 gwq, gws, gwb = q4.quantize_weights(wt, "affine", g.bs, bits=bits)
-                t = time_eager(lambda: q4.gemm("affine", g.bs, gwq, gws, gwb, xq, xs, xsum, y=yy, bits=bits),
+                t = time_graphed(lambda: q4.gemm("affine", g.bs, gwq, gws, gwb, xq, xs, xsum, y=yy, bits=bits),
                                20 if g.M >= 4096 else 50)
                 out[f"{name}_{bits}bit"] = {"gemm_us": round(t * 1e6, 2), "TOPS": round(ops / t / 1e12, 1),
                                             "frac_int8_peak": round(ops / t / 1e12 / INT8_PEAK_TOPS, 4),
@@ -377,7 +385,7 @@ def main():
             g16 = synth.workload("q4_k_gemm_16x4096x14336")
             x16 = torch.from_numpy(synth.gen.activations(g16)).to(dev)
             y16 = torch.empty((16, g16.N), dtype=torch.float32, device=dev)
-            t = time_eager(lambda: q4.q4k_gemm(blocks, x16, g16.N, y=y16), 200)
+            t = time_graphed(lambda: q4.q4k_gemm(blocks, x16, g16.N, y=y16), 200)
             flops = 2.0 * 16 * g16.N * g16.K
             secondary["q4k_gemm_16x4096x14336"] = {
                 "us": round(t * 1e6, 2), "TFLOPS": round(flops / t / 1e12, 2),
@@ -402,7 +410,7 @@ def main():
                 def bw():
                     q4.q4k_gemm_backward(wcopies[it[0] % 8], dyt, g1.K, dx=dxt, work=work)
                     it[0] += 1
-                t = time_eager(bw, 64)
+                t = time_graphed(bw, 64)
                 out[f"q4k_{M}x4096x14336"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(wbytes / t / 1e9, 1),
                                               "TFLOPS": round(2.0 * M * g1.K * g1.N / t / 1e12, 2)}
             del wcopies, blocks
@@ -414,7 +422,7 @@ def main():
                 dxt = torch.empty((M, g1.K), dtype=torch.float32, device=dev)
                 work = torch.empty(int(q4.lib().q4_backward_work_bytes(M, g1.K, g1.N)) // 4, dtype=torch.float32,
                                    device=dev)
-                t = time_eager(lambda: q4.gemm_backward("q4_0", 32, wq, wd, None, dyt, dx=dxt, work=work), 64)
+                t = time_graphed(lambda: q4.gemm_backward("q4_0", 32, wq, wd, None, dyt, dx=dxt, work=work), 64)
                 out[f"q4_0_{M}x4096x14336"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(wbytes / t / 1e9, 1),
                                                "TFLOPS": round(2.0 * M * g1.K * g1.N / t / 1e12, 2)}
         secondary["input_gradient_frozen_weights"] = out

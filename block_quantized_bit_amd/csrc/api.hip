@@ -133,7 +133,7 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, c
     st = check_matmul_ptrs(fmt, wq, wscale, wbias, xq, xs, xsum, y);
     if (st) return st;
     // a few rows: stream every weight block once for all of them
-    if (M <= q4::GEMM_SMALL_MAX_M)
+    if (q4::gemm_small_preferred(M, N))
         return hip_status(q4::launch_gemm_small(M, K, N, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, y, nullptr,
                                                 static_cast<hipStream_t>(stream)));
     return hip_status(q4::launch_gemm(M, K, N, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, y, nullptr,

@@ -43,11 +43,12 @@ namespace {
 constexpr int SW = 8;          // wavefronts per workgroup
 constexpr int SNT = 64 * SW;   // threads per workgroup
 constexpr int SN = 16;         // output columns per workgroup
-// K per chunk staged in LDS: 2048 with one 16-row tile, 1024 with two (the
-// activation codes of a chunk and two chunks of loads in flight stay within
-// the register and LDS budget).
-template <int MT>
-constexpr int chunk_k() { return MT == 1 ? 2048 : 1024; }
+// K per chunk staged in LDS: 2048 with one 16-row tile, 1024 with two, 512
+// with four (1024 for 128-weight groups: a wavefront's share of a chunk holds
+// whole groups). The activation codes of a chunk and two chunks of loads in
+// flight then stay within the register and LDS budget.
+template <int MT, int G>
+constexpr int chunk_k() { return MT == 1 ? 2048 : (MT == 2 || G == 128) ? 1024 : 512; }
 constexpr int RSRC_WORD3 = 0x00020000;  // gfx9 raw buffer descriptor: 32-bit data format
 constexpr uint32_t OUT = 0x80000000u;   // beyond every buffer range: reads as zero
 
@@ -57,16 +58,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 
 // Code bytes per weight row and chunk: the main part (nibbles, or bytes for
 // 8-bit codes) and, for 6-bit codes, the high 2-bit plane after it.
-template <int MT, int BITS>
-constexpr int main_bytes() { return BITS == 8 ? chunk_k<MT>() : chunk_k<MT>() / 2; }
-template <int MT, int BITS>
-constexpr int plane_bytes() { return BITS == 6 ? chunk_k<MT>() / 4 : 0; }
+template <int MT, int G, int BITS>
+constexpr int main_bytes() { return BITS == 8 ? chunk_k<MT, G>() : chunk_k<MT, G>() / 2; }
+template <int MT, int G, int BITS>
+constexpr int plane_bytes() { return BITS == 6 ? chunk_k<MT, G>() / 4 : 0; }
 
 template <int G, int MT, int BITS>
 struct SmallLds {
-    static constexpr int KC = chunk_k<MT>();
+    static constexpr int KC = chunk_k<MT, G>();
     static constexpr int GPC = KC / G;  // groups per chunk
-    uint8_t w[SN][main_bytes<MT, BITS>() + plane_bytes<MT, BITS>() + 16];  // codes (16 bytes of padding per row)
+    uint8_t w[SN][main_bytes<MT, G, BITS>() + plane_bytes<MT, G, BITS>() + 16];  // codes (16 bytes of padding per row)
     uint8_t a[16 * MT][KC + 16];        // activation codes of the chunk
     float xs[GPC][16 * MT];             // activation scales, group-major
     float xb[GPC][16 * MT];             // xs * xsum (affine)
@@ -87,12 +88,13 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
     constexpr bool AFF = FMT == 1;
     constexpr int MR = 16 * MT;     // rows covered by the MFMA tiles
     using L = SmallLds<G, MT, BITS>;
-    constexpr int MB = main_bytes<MT, BITS>(), PB = plane_bytes<MT, BITS>();
+    constexpr int MB = main_bytes<MT, G, BITS>(), PB = plane_bytes<MT, G, BITS>();
     constexpr int KC = L::KC;
     constexpr int GPC = L::GPC;
     constexpr int SPW = KC / 32 / SW;  // MFMA steps per wavefront per chunk
     static_assert(SPW % SPG == 0, "a wavefront's share of a chunk holds whole groups");
-    constexpr int W_CH = SN * MB / 16 / SNT;           // 16-byte code loads per thread per chunk
+    static_assert((16 * MT * KC / 16) % SNT == 0, "activation staging covers the chunk exactly");
+    constexpr int W_CH = (SN * MB / 16 + SNT - 1) / SNT;  // 16-byte code loads per thread per chunk (rounded up)
     constexpr int P_CH = (SN * PB / 16 + SNT - 1) / SNT;  // 16-byte high-plane loads (6 bits)
     constexpr int CPS = BITS == 8 ? 16 : 32;           // codes per 16 bytes of the main part
     constexpr int A_CH = MR * KC / 16 / SNT;           // 16-byte activation loads per thread per chunk (4 / 8)
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
 #pragma unroll
         for (int i = 0; i < W_CH; ++i) {
             const int idx = tid + SNT * i, r = idx / (MB / 16), seg = idx % (MB / 16);  // 16-byte segment
-            const bool in = n0 + r < N && k0 + CPS * seg < K;
+            const bool in = idx < SN * MB / 16 && n0 + r < N && k0 + CPS * seg < K;
             const uint32_t rowb = BITS == 8 ? (uint32_t)K : (uint32_t)(K / 2);
             rw[B][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 r_b, in ? (uint32_t)((n0 + r) * rowb + 16 * seg) : OUT, BITS == 8 ? k0 : k0 / 2, 0));
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(SNT, 1) void gemm_small_kernel(int M, int K, int N,
 #pragma unroll
         for (int i = 0; i < W_CH; ++i) {
             const int idx = tid + SNT * i, r = idx / (MB / 16), seg = idx % (MB / 16);
-            *reinterpret_cast<uint4*>(&S.w[r][16 * seg]) = rw[B][i];
+            if (idx < SN * MB / 16) *reinterpret_cast<uint4*>(&S.w[r][16 * seg]) = rw[B][i];
         }
 #pragma unroll
         for (int i = 0; i < P_CH; ++i) {
@@ -343,7 +345,8 @@ hipError_t launch_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale
                       const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                       hipStream_t stream) {
     if (M <= 16) return launch_mt<FMT, G, 1, BITS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    return launch_mt<FMT, G, 2, BITS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (M <= 32) return launch_mt<FMT, G, 2, BITS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return launch_mt<FMT, G, 4, BITS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
 }
 
 template <int G>

@@ -33,7 +33,16 @@ hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, int bits, const uin
 // Few-row GEMM (1 <= M <= GEMM_SMALL_MAX_M): every weight block is read once
 // for all rows (16x16x32 int8 MFMA, K chunks staged in LDS and split over the
 // wavefronts of a workgroup). Same arguments as launch_gemm.
-constexpr int GEMM_SMALL_MAX_M = 32;
+constexpr int GEMM_SMALL_MAX_M = 64;
+// Which kernel q4_gemm takes: the few-row kernel up to 32 rows, and up to 64
+// rows while N <= 8192. Each of its workgroups (16 columns) reads all M x K
+// activation codes, so for 33..64 rows and wide N the tiled kernel is faster
+// (measured at K = 4096: N = 4096 few-row 11.6-15.3 us against tiled 31-52 us;
+// N = 14336 few-row 39-53 us against tiled 32-45 us).
+constexpr int GEMM_SMALL_WIDE_N = 8192;
+inline bool gemm_small_preferred(int M, int N) {
+    return M <= 32 || (M <= GEMM_SMALL_MAX_M && N <= GEMM_SMALL_WIDE_N);
+}
 hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream);

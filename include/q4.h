@@ -145,11 +145,13 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
  *   M <= 4 with 4-bit codes: the decode GEMV's weight stream, each weight
  *     chunk unpacked once and dotted (v_dot4) with the codes of every row,
  *     which are held in registers.
- *   other M <= 32: every weight block is read once for all rows (16x16x32
- *     int8 MFMA, 16 output columns per workgroup, K chunks staged in LDS and
- *     split over its wavefronts). tract PR #2432 measures decode-sized
- *     products as weight streams; MLX PR #4802 leaves its int8 path below
- *     M = 32.
+ *   other M <= 32, and 33 <= M <= 64 with N <= 8192: every weight block is
+ *     read once for all rows (16x16x32 int8 MFMA on one, two or four 16-row
+ *     tiles, 16 output columns per workgroup, K chunks staged in LDS and
+ *     split over its wavefronts; each workgroup reads all M x K activation
+ *     codes, which is why wide N goes to the tiled kernel above 32 rows).
+ *     tract PR #2432 measures decode-sized products as weight streams; MLX
+ *     PR #4802 leaves its int8 path below M = 32.
  *   otherwise: 128 x 128 output tiles on 32x32x32 int8 MFMA, one 32-weight
  *     block per K step. For 4- and 6-bit codes this kernel takes each
  *     block's integer sum into float through an exponent bias, which needs
@@ -164,8 +166,9 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
 /*
  * Debug view of the exact integer partials computed inside q4_gemv
  * (path Q4_PATH_GEMV, needs M == 1) or q4_gemm (Q4_PATH_GEMM: the tiled
- * kernel, any row count; Q4_PATH_SMALL: the few-row kernels that q4_gemm
- * takes for m1 - m0 rows, m1 - m0 <= 32, else Q4_ERR_RANGE): the same kernels, compiled
+ * kernel, any row count; Q4_PATH_SMALL: the few-row kernels, which q4_gemm
+ * takes as described there, for m1 - m0 <= 64 rows at any N, else
+ * Q4_ERR_RANGE): the same kernels, compiled
  * with the partials store in place of the float epilogue.
  * partials [(m1-m0)][N][K/bs] int32 for rows m0 <= m < m1:
  *   Q4_0:   sum_{k in b} (q - 8) * xq[m][k]

@@ -127,8 +127,8 @@ def test_debug_partials_validation():
     assert f(*args) == RANGE                             # GEMV path needs one row
     args = list(base); args[12] = None
     assert f(*args) == NULL
-    # few-row kernel: at most 32 rows
-    big = [2, 40, 128, 8, 32, 0, 4, A, A, A, 0, 33, A, None]
+    # few-row kernel: at most 64 rows
+    big = [2, 80, 128, 8, 32, 0, 4, A, A, A, 0, 65, A, None]
     assert f(*big) == RANGE
 
 

@@ -239,9 +239,11 @@ def test_gemv_ragged(fmt, bs, K, N):
 @pytest.mark.parametrize("fmt,bs,M,K,N", [
     ("q4_0", 32, 1, 32, 1), ("q4_0", 32, 3, 96, 33), ("q4_0", 32, 65, 160, 1537), ("q4_0", 32, 257, 416, 130),
     ("affine", 64, 1, 64, 5), ("affine", 64, 129, 320, 255), ("affine", 128, 200, 384, 131),
-    ("affine", 128, 64, 4224, 64),
+    ("affine", 128, 65, 4224, 64),
+    # 33..64 rows with N > 8192: the tiled kernel (the few-row one above 32 rows takes N <= 8192)
+    ("q4_0", 32, 48, 256, 8224),
     # few tiles and at least 8 K stages: K split over two wavefront groups per workgroup
-    ("affine", 64, 33, 2048, 129), ("q4_0", 32, 200, 1024, 100),
+    ("affine", 64, 65, 2048, 129), ("q4_0", 32, 200, 1024, 100),
 ])
 def test_gemm_ragged(fmt, bs, M, K, N):
     print(f"case gemm {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
@@ -290,11 +292,15 @@ def test_gemm_deterministic():
     assert torch.equal(y1, y2)
 
 
-# ---------------------------------------------------------------- few-row GEMM (M <= 32)
+# ---------------------------------------------------------------- few-row GEMM (M <= 64)
 
 SMALL_CASES = [("q4_0", 32, 2, 416, 37), ("q4_0", 32, 16, 96, 17), ("q4_0", 32, 17, 4096, 33),
                ("q4_0", 32, 32, 8224, 16), ("affine", 64, 5, 320, 31), ("affine", 64, 32, 4096, 48),
                ("affine", 128, 3, 14336, 21), ("affine", 128, 24, 384, 129),
+               # 33 to 64 rows: four 16-row tiles; 512-wide K chunks (Q4_0, g64) and 1024-wide (g128),
+               # ragged last chunk, rows and columns
+               ("q4_0", 32, 33, 544, 20), ("q4_0", 32, 64, 1632, 33), ("affine", 64, 48, 1088, 37),
+               ("affine", 64, 64, 4096, 17), ("affine", 128, 40, 2176, 70), ("affine", 128, 64, 1024, 16),
                # up to 4 rows of 4-bit codes: the GEMV-shaped kernel (several K passes, pass tails,
                # ragged N, and N smaller than a workgroup's rows)
                ("affine", 64, 4, 4160, 45), ("affine", 128, 1, 8320, 19), ("q4_0", 32, 3, 12320, 7),
@@ -315,12 +321,12 @@ def test_small_partials_bit_exact(fmt, bs, M, K, N):
 def test_small_gemm_ragged(fmt, bs, M, K, N):
     print(f"case small gemm {fmt} bs={bs} M={M} K={K} N={N}", flush=True)
     wts, act = _partials_case(fmt, bs, M, K, N, 7 * M + K + N)
-    y = q4.gemm(fmt, bs, *_wts_dev(fmt, wts), *[to_dev(a) for a in act])   # M <= 32: the few-row kernel
+    y = q4.gemm(fmt, bs, *_wts_dev(fmt, wts), *[to_dev(a) for a in act])   # M <= 64: the few-row kernel
     _sync()
     assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
 
 
-@pytest.mark.parametrize("M", [2, 4, 8, 16, 32])
+@pytest.mark.parametrize("M", [2, 4, 8, 16, 32, 64])
 def test_small_gemm_decode_rows(M):
     # the decode workload's weights against M rows drawn like its activation vector
     print(f"case small gemm q4_0 decode rows M={M}", flush=True)
@@ -335,16 +341,16 @@ def test_small_gemm_decode_rows(M):
 
 
 def test_small_gemm_dispatch_boundary():
-    # 32 rows take the few-row kernel, 33 the tiled one; both against the oracle
-    print("case small/tiled boundary M=32,33", flush=True)
-    wts, act = _partials_case("affine", 64, 33, 1024, 200, 4242)
+    # 64 rows take the few-row kernel (four 16-row tiles), 65 the tiled one, 32 and
+    # 33 the two- and four-tile few-row kernels; all against the oracle
+    print("case small/tiled boundary M=32,33,64,65", flush=True)
+    wts, act = _partials_case("affine", 64, 65, 1024, 200, 4242)
     g = _wts_dev("affine", wts)
     ref = _oracle_y("affine", wts, act, 1024, 200, 64)
-    y33 = q4.gemm("affine", 64, *g, *[to_dev(a) for a in act])
-    y32 = q4.gemm("affine", 64, *g, *[to_dev(a[:32]) for a in act])
-    _sync()
-    assert rel_rms(to_np(y33), ref) <= TOL
-    assert rel_rms(to_np(y32), ref[:32]) <= TOL
+    for m in (32, 33, 64, 65):
+        y = q4.gemm("affine", 64, *g, *[to_dev(a[:m]) for a in act])
+        _sync()
+        assert rel_rms(to_np(y), ref[:m]) <= TOL, m
 
 
 @pytest.mark.parametrize("fmt,bs,M,N", [("q4_0", 32, 32, 16), ("affine", 64, 17, 20)])
@@ -416,7 +422,7 @@ def test_bits_partials_bit_exact(bits, g, M, K, N):
     got = q4.debug_partials("gemm", "affine", g, *args, bits=bits)
     _sync()
     assert np.array_equal(to_np(got), ref)
-    if M <= 32:
+    if M <= 64:
         gs_ = q4.debug_partials("small", "affine", g, *args, bits=bits)
         _sync()
         assert np.array_equal(to_np(gs_), ref)
@@ -504,8 +510,8 @@ def test_gemm_packed_ragged(fmt, bs, M, K, N):
     assert np.array_equal(to_np(xs_gm).T.view(np.uint32), act[1].view(np.uint32))
     assert np.array_equal(to_np(xsum_gm).T, act[2])
     assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
-    if M > 32:
-        # same tiled kernel arithmetic as the unpacked GEMM: identical results
+    if M > 64:
+        # same tiled kernel arithmetic as the unpacked GEMM (which takes the tiled kernel above 64 rows)
         yu = q4.gemm(fmt, bs, *g, xq, *[to_dev(a) for a in act[1:]])
         _sync()
         assert torch.equal(y, yu)
