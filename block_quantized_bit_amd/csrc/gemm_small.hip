@@ -1,5 +1,7 @@
-// W4A8 GEMM for a few activation rows (M <= 32): the regime between the
-// decode GEMV (M = 1) and the tiled prefill GEMM.
+// W4A8 GEMM for a few activation rows (M <= 64): the regime between the
+// decode GEMV (M = 1) and the tiled prefill GEMM. q4_gemm takes it up to 32
+// rows, and for 33..64 rows when N <= 8192 (each workgroup reads all M x K
+// activation codes, so wider products go to the tiled kernel).
 //
 // tract PR #2432 (follow-up decode measurements): the weights dominate the
 // traffic of a decode-sized product, so they must be streamed once.
@@ -11,13 +13,13 @@
 // which is faster there; the kernel below covers the rest.
 //
 // A workgroup owns 16 output columns and all M rows, so every weight block is
-// read once for all rows. K is walked in chunks of 2048: the workgroup copies
-// the chunk's packed codes (16 rows x 1 KB), activation codes (M rows x 2 KB)
-// and activation scales into LDS with coalesced 128-bit loads (the next
-// chunk's loads are in flight while this one is computed), then its 8
-// wavefronts split the chunk's 64 K steps; each runs v_mfma_i32_16x16x32_i8
-// (16 rows x 16 columns x one 32-weight block) per step, with one or two
-// 16-row tiles. The wavefronts' float partial sums are added in LDS in a
+// read once for all rows. K is walked in chunks (2048, 1024 or 512 wide, see
+// chunk_k): the workgroup copies the chunk's packed codes (16 rows), activation
+// codes (M rows) and activation scales into LDS with coalesced 128-bit loads
+// (the next chunk's loads are in flight while this one is computed), then its
+// 8 wavefronts split the chunk's K steps; each runs v_mfma_i32_16x16x32_i8
+// (16 rows x 16 columns x one 32-weight block) per step, with one, two or
+// four 16-row tiles. The wavefronts' float partial sums are added in LDS in a
 // fixed order (no atomics, so results do not depend on scheduling).
 //
 // Operands of the 16x16x32 int8 MFMA (lane l, q = l / 16): A holds row l % 16
