@@ -253,6 +253,29 @@ def test_gemm_ragged(fmt, bs, M, K, N):
     assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
 
 
+@pytest.mark.parametrize("M", [1, 8, 65])
+def test_gemm_large_scales(M):
+    # affine scales and biases times 2^90 (bf16 exponent field + 90): the tiled
+    # kernel (M = 65) takes each group's integer sum into float through an
+    # exponent bias and needs |scale| < 2^104; the few-row kernels (M = 1, 8)
+    # convert directly. All three against the oracle, with finite outputs.
+    print(f"case gemm large scales M={M}", flush=True)
+    K, N = 512, 130
+    (wq, ws, wb), act = _partials_case("affine", 128, M, K, N, 777 + M)
+
+    def up(bits):
+        bits = bits.copy()
+        nz = (bits & 0x7FFF) != 0
+        bits[nz] = bits[nz] + np.uint16(90 << 7)
+        return bits
+    wts = (wq, up(ws), up(wb))
+    y = q4.gemm("affine", 128, *_wts_dev("affine", wts), *[to_dev(a) for a in act])
+    _sync()
+    got = to_np(y)
+    assert np.all(np.isfinite(got))
+    assert rel_rms(got, _oracle_y("affine", wts, act, K, N, 128)) <= TOL
+
+
 def test_gemm_minilm_workload_full():
     print("case gemm q4_0 64x384x1536", flush=True)
     wl, _, _, act, wts = workload_data("q4_0_minilm_64x384x1536")
