@@ -423,7 +423,9 @@ def _bits_case(bits, g, M, K, N, seed):
 
 
 BITS_CASES = [(6, 64, 3, 320, 37), (6, 128, 130, 384, 131), (6, 64, 17, 4096, 65), (8, 64, 2, 192, 33),
-              (8, 128, 129, 512, 257), (8, 64, 32, 4096, 48), (8, 128, 200, 1152, 64), (6, 64, 40, 1024, 70)]
+              (8, 128, 129, 512, 257), (8, 64, 32, 4096, 48), (8, 128, 200, 1152, 64), (6, 64, 40, 1024, 70),
+              # four-tile few-row kernel: 8-bit codes in 512- (g64) and 1024-wide (g128) K chunks
+              (8, 64, 56, 640, 40), (8, 128, 64, 1152, 24), (6, 128, 36, 2304, 33)]
 
 
 @pytest.mark.parametrize("bits,g", [(6, 64), (6, 128), (8, 64), (8, 128)])
