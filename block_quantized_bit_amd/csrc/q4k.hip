@@ -217,34 +217,100 @@ __global__ __launch_bounds__(256) void q4k_gemv_long_kernel(int K, int N, const 
     if (lane == 0) y[n] = acc;
 }
 
-// GEMM on the float32 matrix cores (v_mfma_f32_16x16x4_f32). A workgroup of
-// W x KP wavefronts covers 16 activation rows x 16 W weight rows; wavefront
-// (w, p) owns weight rows 16 w .. 16 w + 15 and the p-th of KP contiguous
-// ranges of super-blocks (more wavefronts per SIMD to overlap the dependent
-// MFMA chains), and the KP partial sums are added in LDS in a fixed order at
-// the end. For every super-block the 16 x 256 activation tile of a K range is
-// staged in LDS; lane l dequantizes chunk h = l / 16 (64 weights: 32 low
-// nibbles of sub-block 2h, then 32 high nibbles of sub-block 2h + 1) of weight
-// row l % 16 and feeds one weight per MFMA; the 4 lane groups are the MFMA's
-// 4 K slots, so one MFMA takes weights 64h + t of the block for h = 0..3.
-// The loads of the next super-block (activation tile and the lane's header
-// and codes) are in registers while the current one is computed, and the
-// activation tiles are double-buffered in LDS, so a super-block costs one
-// barrier. All loads are buffer loads with no branch around them: rows past M
-// or N and super-blocks past a range read zero.
-constexpr int XS_STRIDE = QK + 4;  // floats; keeps 16-byte alignment and spreads rows over the banks
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Largest value over the 64 lanes of a wavefront; every lane receives it.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Sum over aligned groups of 8 lanes; every lane of a group receives it.
+__device__ __forceinline__ float sum8(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+// Two codes (nibbles in bits 0..3 and 16..19 of t) as an exact f16 pair:
+// 0x6400 | q is the half 1024 + q, and subtracting 1024 leaves q.
+__device__ __forceinline__ uint32_t code_pair_f16(uint32_t t) {
+    v2h h = __builtin_bit_cast(v2h, (t & 0x000F000Fu) | 0x64006400u);
+    h = h - v2h{(_Float16)1024.0f, (_Float16)1024.0f};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// The 16 codes of 8 qs bytes as two f16 MFMA operands: low nibbles (byte i is
+// weight k = i of the lane's 8 in one sub-block) and high nibbles (the same k
+// in the next sub-block).
+__device__ __forceinline__ void codes_f16(uint2 cw, v8h& blo, v8h& bhi) {
+    const uint32_t p0 = __builtin_amdgcn_perm(0u, cw.x, 0x0C010C00u);  // bytes 0, 1 into the two halves
+    const uint32_t p1 = __builtin_amdgcn_perm(0u, cw.x, 0x0C030C02u);  // bytes 2, 3
+    const uint32_t p2 = __builtin_amdgcn_perm(0u, cw.y, 0x0C010C00u);
+    const uint32_t p3 = __builtin_amdgcn_perm(0u, cw.y, 0x0C030C02u);
+    blo = __builtin_bit_cast(v8h, make_uint4(code_pair_f16(p0), code_pair_f16(p1), code_pair_f16(p2), code_pair_f16(p3)));
+    bhi = __builtin_bit_cast(v8h, make_uint4(code_pair_f16(p0 >> 4), code_pair_f16(p1 >> 4), code_pair_f16(p2 >> 4),
+                                             code_pair_f16(p3 >> 4)));
+}
+
+// GEMM on the f16 matrix cores (v_mfma_f32_16x16x32_f16), float32-accurate.
+// Per sub-block the product is factored as in the GEMV,
+//   sum_k (d sc q - dmin m) x = (d sc) sum_k q x - (dmin m) sum_k x,
+// and sum_k q x is taken on the matrix cores: a code is an exact f16, and each
+// activation enters as two f16 halves, hi = f16(x') and lo = f16(x' - hi), of
+// x' = x * 2^e, the row's values over the super-block scaled by a power of two
+// that puts their largest magnitude in [2^14, 2^15) (inside the f16 range, and
+// lo stays a normal number for all but the row's tiny values; the scale is at
+// most 2^126, so only rows whose largest magnitude in a super-block is below
+// 2^-112 lose relative precision). hi + lo carries
+// 22 of x's 24 significant bits, every code x half product is exact in f32, so
+// the sum differs from the float32 one by rounding only; the result is scaled
+// back by 2^-e (exact).
+//
+// A workgroup of W x KP wavefronts covers 16 activation rows x 16 W weight
+// rows; wavefront (w, p) owns weight rows 16 w .. 16 w + 15 and the p-th of KP
+// contiguous ranges of super-blocks, and the KP partial sums are added in LDS
+// in a fixed order at the end. For every super-block the workgroup stages the
+// 16 x 256 activation tile of each range in LDS as the hi and lo halves plus
+// per-row sub-block sums and the row's 2^-e. Lane l of a wavefront holds
+// weight row l % 16; its operands for k = 8 (l / 16) .. +7 of a sub-block are 8
+// bytes of qs (low nibbles: sub-block 2c, high nibbles: 2c + 1, chunk c), so
+// one sub-block is two MFMAs (hi, lo). The next super-block's loads are in
+// registers while the current one is computed, and the staged tiles are
+// double-buffered, so a super-block costs one barrier. All loads are buffer
+// loads with no branch around them: rows past M or N and super-blocks past a
+// range read zero.
+constexpr int XR = QK + 8;  // halves per staged row: 16-byte aligned, rows 4 banks apart
+
+template <int W, int KP>
+struct Q4kStage {
+    v8h hi[2][16 * XR / 8];  // [buffer][row * XR / 8 + k / 8]
+    v8h lo[2][16 * XR / 8];
+    float sum[2][8][16];     // [buffer][sub-block][row]: sum of the scaled activations
+    float inv[2][16];        // [buffer][row]: 2^-e
+};
 
 template <int W, int KP>
 __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ blocks,
                                                                const float* __restrict__ x, float* __restrict__ y) {
     constexpr int NTH = 64 * W;             // threads of one K range
     constexpr int XCH = 16 * QK / 4 / NTH;  // float4 of the activation tile per thread (16 / W)
-    __shared__ __attribute__((aligned(16))) float xs[KP][2][16 * XS_STRIDE];
+    static_assert(XCH * NTH == 16 * QK / 4, "staging covers the tile");
+    __shared__ Q4kStage<W, KP> st[KP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = wave / W, tp = tid - p * NTH;  // K range, thread within the range's group
     const int m0 = blockIdx.y * 16;
     const int n = blockIdx.x * (16 * W) + (wave % W) * 16 + (lane & 15);
-    const int h = lane >> 4;
+    const int q = lane >> 4;
     const int nsb = K >> 8;
     const int per = (nsb + KP - 1) / KP;  // super-blocks per range
     const int sb0 = p * per, sb1 = min(nsb, sb0 + per);
@@ -260,7 +326,8 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
     const uint32_t ow = (n < N) ? (uint32_t)((size_t)n * nsb * BLOCK_BYTES) : OUT;
 
     float4 rx[XCH];
-    uint4 rh, rq0, rq1;
+    uint4 rh;
+    uint2 rq[4];
     auto load = [&](int sb) {  // super-blocks past the range read zero
         const bool in = sb < sb1;
 #pragma unroll
@@ -269,72 +336,105 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
                                                                                      in ? sb * QK * 4 : 0, 0));
         const uint32_t o = in ? ow : OUT, so = in ? (uint32_t)(sb * BLOCK_BYTES) : 0u;
         rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, so, 0));
-        rq0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 16 + 32 * h, so, 0));
-        rq1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 32 + 32 * h, so, 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            rq[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  r_w, o == OUT ? OUT : o + 16 + 32 * c + 8 * q, so, 0));
     };
-    auto store_x = [&](float* buf) {
+    // Stage the tile in buffer b: row r = wave-in-group + W i is held by the 64
+    // lanes of one wavefront (lane = float4 index), so its largest magnitude
+    // and its sub-block sums are wavefront and 8-lane reductions.
+    auto stage = [&](int b) {
+        Q4kStage<W, KP>& S = st[p];
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int idx = tp + NTH * i, r = idx >> 6, c4 = idx & 63;
-            *reinterpret_cast<float4*>(&buf[r * XS_STRIDE + 4 * c4]) = rx[i];
+            const float4 v = rx[i];
+            const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            // mx = f * 2^E, f in [0.5, 1) (E = -126 below the normal range); scale by 2^(15 - E),
+            // at most 2^126 so that the scale and its inverse stay normal floats
+            const int E = max((int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF) - 126, -111);
+            const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 15 - E) << 23);
+            const float xs0 = v.x * sc, xs1 = v.y * sc, xs2 = v.z * sc, xs3 = v.w * sc;
+            const _Float16 h0 = (_Float16)xs0, h1 = (_Float16)xs1, h2 = (_Float16)xs2, h3 = (_Float16)xs3;
+            const _Float16 l0 = (_Float16)(xs0 - (float)h0), l1 = (_Float16)(xs1 - (float)h1);
+            const _Float16 l2 = (_Float16)(xs2 - (float)h2), l3 = (_Float16)(xs3 - (float)h3);
+            typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<v4h*>(reinterpret_cast<_Float16*>(S.hi[b]) + r * XR + 4 * c4) = v4h{h0, h1, h2, h3};
+            *reinterpret_cast<v4h*>(reinterpret_cast<_Float16*>(S.lo[b]) + r * XR + 4 * c4) = v4h{l0, l1, l2, l3};
+            const float ssum = sum8((xs0 + xs1) + (xs2 + xs3));
+            if ((c4 & 7) == 0) S.sum[b][c4 >> 3][r] = ssum;
+            if (c4 == 0) S.inv[b][r] = __builtin_bit_cast(float, (uint32_t)(127 - 15 + E) << 23);
         }
     };
 
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
     load(sb0);
-    store_x(xs[p][0]);
-    uint4 hdr = rh, q0 = rq0, q1 = rq1;
+    stage(0);
+    uint4 hdr = rh;
+    uint2 cw[4] = {rq[0], rq[1], rq[2], rq[3]};
     load(sb0 + 1);
+    const int row = lane & 15;  // activation row of this lane's A operands
     for (int it = 0; it < per; ++it) {  // the same trip count in every range (past its end: zeros)
         const int sb = sb0 + it;
         __syncthreads();  // tile it is complete; every wavefront is done with the other buffer
-        store_x(xs[p][(it + 1) & 1]);
-        const uint4 ch = hdr, c0 = q0, c1 = q1;
+        stage((it + 1) & 1);
+        const uint4 ch = hdr;
+        const uint2 c0 = cw[0], c1 = cw[1], c2 = cw[2], c3 = cw[3];
         hdr = rh;
-        q0 = rq0;
-        q1 = rq1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cw[c] = rq[c];
         load(sb + 2);
+        const int b = it & 1;
+        const Q4kStage<W, KP>& S = st[p];
         const float d = half_to_float(ch.x & 0xFFFFu), dmin = half_to_float(ch.x >> 16);
-        float sc0, sc1, mm0, mm1;
-        q4k_pair_scales(ch, h, sc0, sc1, mm0, mm1);
-        const float ds0 = d * sc0, dm0 = dmin * mm0, ds1 = d * sc1, dm1 = dmin * mm1;
-        const uint32_t qw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        const float* xr = &xs[p][it & 1][(lane & 15) * XS_STRIDE + 64 * h];
+        const uint2 cc[4] = {c0, c1, c2, c3};
+        v4f part = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t4 = 0; t4 < 8; ++t4) {  // low nibbles: weights 64h + 0..31
-            const float4 xv = *reinterpret_cast<const float4*>(xr + 4 * t4);
-            const uint32_t ql = nibbles_lo(qw[t4]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, fmaf(ds0, byte_f(ql, 0), -dm0), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, fmaf(ds0, byte_f(ql, 1), -dm0), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, fmaf(ds0, byte_f(ql, 2), -dm0), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, fmaf(ds0, byte_f(ql, 3), -dm0), acc, 0, 0, 0);
-        }
+        for (int c = 0; c < 4; ++c) {
+            float sc0, sc1, mm0, mm1;
+            q4k_pair_scales(ch, c, sc0, sc1, mm0, mm1);
+            v8h blo, bhi;
+            codes_f16(cc[c], blo, bhi);
+            const v8h* H = S.hi[b] + (row * XR + 64 * c + 8 * q) / 8;
+            const v8h* L = S.lo[b] + (row * XR + 64 * c + 8 * q) / 8;
+            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+            v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(H[0], blo, z, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(L[0], blo, d0, 0, 0, 0);
+            v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(H[4], bhi, z, 0, 0, 0);  // k + 32: sub-block 2c + 1
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(L[4], bhi, d1, 0, 0, 0);
+            const v4f s0 = *reinterpret_cast<const v4f*>(&S.sum[b][2 * c][4 * q]);
+            const v4f s1 = *reinterpret_cast<const v4f*>(&S.sum[b][2 * c + 1][4 * q]);
+            const float a0 = d * sc0, a1 = d * sc1, e0 = dmin * mm0, e1 = dmin * mm1;
 #pragma unroll
-        for (int t4 = 0; t4 < 8; ++t4) {  // high nibbles: weights 64h + 32..63
-            const float4 xv = *reinterpret_cast<const float4*>(xr + 32 + 4 * t4);
-            const uint32_t qh = nibbles_hi(qw[t4]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.x, fmaf(ds1, byte_f(qh, 0), -dm1), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.y, fmaf(ds1, byte_f(qh, 1), -dm1), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.z, fmaf(ds1, byte_f(qh, 2), -dm1), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xv.w, fmaf(ds1, byte_f(qh, 3), -dm1), acc, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) {
+                part[r] = fmaf(a0, d0[r], part[r]);
+                part[r] = fmaf(-e0, s0[r], part[r]);
+                part[r] = fmaf(a1, d1[r], part[r]);
+                part[r] = fmaf(-e1, s1[r], part[r]);
+            }
         }
+        const v4f iv = *reinterpret_cast<const v4f*>(&S.inv[b][4 * q]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = fmaf(iv[r], part[r], acc[r]);
     }
-    // add the K ranges in order (p = 0, 1, ...) through LDS, reusing the tiles
+    // add the K ranges in order (p = 0, 1, ...) through LDS, reusing the staging memory
     if (KP > 1) {
         __syncthreads();
-        float* part = &xs[0][0][0];  // [KP][W][64 lanes][4]
-        if (p > 0) *reinterpret_cast<v4f*>(&part[((p * W + wave % W) * 64 + lane) * 4]) = acc;
+        float* pbuf = reinterpret_cast<float*>(&st[0]);  // [KP][W][64 lanes][4]
+        if (p > 0) *reinterpret_cast<v4f*>(&pbuf[((p * W + wave % W) * 64 + lane) * 4]) = acc;
         __syncthreads();
         if (p == 0) {
 #pragma unroll
-            for (int q = 1; q < KP; ++q) acc += *reinterpret_cast<const v4f*>(&part[((q * W + wave % W) * 64 + lane) * 4]);
+            for (int k2 = 1; k2 < KP; ++k2)
+                acc += *reinterpret_cast<const v4f*>(&pbuf[((k2 * W + wave % W) * 64 + lane) * 4]);
         }
     }
     // D layout: lane holds column lane%16, rows 4*(lane/16) + r
     if (p == 0 && n < N) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = m0 + 4 * h + r;
+            const int m = m0 + 4 * q + r;
             if (m < M) y[(size_t)m * N + n] = acc[r];
         }
     }

@@ -184,7 +184,12 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits,
  * Q4_K fused-dequant GEMV (M must be 1) and GEMM (any M >= 1) with float32
  * activations (C-Kernel-Engine gemm_kernels_q4k.c: gemv_q4_k_ref computes
  * sum_k (d*sc*q - dmin*m) * x per output row; gemm_q4_k_ref is one GEMV per
- * activation row). Dequantized weights live only in registers.
+ * activation row). Dequantized weights live only in registers. q4k_gemm
+ * takes sum_k q * x per 32-weight sub-block on the f16 matrix cores: codes
+ * are exact f16, activations enter as two f16 halves of x scaled by a power
+ * of two per row and 256-weight super-block, so the result is the float32
+ * one up to rounding (for finite activations; a row whose largest magnitude
+ * in a super-block is below 2^-112 loses relative precision there).
  * blocks [N][K/256] x 144 bytes (16-byte aligned), x [M][K] float32
  * (16-byte aligned), y [M][N] float32. K must be a multiple of 256. The
  * kernels address blocks and x with 32-bit byte offsets: N*(K/256)*144 and

@@ -638,6 +638,28 @@ def test_q4k_gemv_workload():
     assert rel_rms(to_np(y)[ms, ns], ref) <= TOL
 
 
+def test_q4k_gemm_row_magnitudes():
+    # The GEMM takes activations through the f16 matrix cores as scaled hi/lo
+    # halves, with a power-of-two scale per row and super-block: rows far
+    # outside the f16 range (1e20, 1e-20, 1e-33), near its top (3e4), and a row
+    # whose super-blocks differ by 1e12 must each match the oracle on their own.
+    print("case q4k gemm row magnitudes", flush=True)
+    K, N = 768, 70
+    rng = np.random.default_rng(4321)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    blocks = oracle.quantize_q4k(w)
+    scales = np.array([1e-20, 1e-5, 1.0, 3e4, 1e5, 1e20, 7.0, 1e-33], dtype=np.float64)
+    x = (rng.standard_normal((8, K)) * scales[:, None]).astype(np.float32)
+    x[6, 256:512] *= np.float32(1e12)   # super-block 1 of row 6: 1e12 x the others
+    ref = oracle.q4k_gemm(blocks, x, K, N)
+    y = q4.q4k_gemm(to_dev(blocks), to_dev(x), N)
+    _sync()
+    got = to_np(y)
+    assert np.all(np.isfinite(got))
+    for m in range(8):
+        assert rel_rms(got[m], ref[m]) <= TOL, m
+
+
 def test_q4k_gemm_workload():
     print("case q4k gemm 16x4096x14336", flush=True)
     wl = synth.workload("q4_k_gemm_16x4096x14336")
