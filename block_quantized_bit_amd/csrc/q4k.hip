@@ -446,17 +446,26 @@ hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, flo
     const uint8_t* b = static_cast<const uint8_t*>(blocks);
     const int units = K >> 5;
     const int upl = (units + 63) / 64;
-    // one row per pass (115 registers: 4 wavefronts per SIMD) and 1024
-    // workgroups of 4 wavefronts: at 4096 x 14336 each wavefront walks 4 rows,
-    // the next one's loads in flight (measured 10.9 us against 11.3 us for
-    // 2 rows per pass and 2048 workgroups)
+    // K <= 4096: two rows per pass, and as many workgroups as give every
+    // wavefront a single pass (at 4096 x 14336: 1792 workgroups, 149
+    // registers, 10.4-10.6 us against 11.4-11.9 us for one row per pass over
+    // 1024 workgroups in the same runs). Longer rows keep one row per pass:
+    // two would not fit the registers beside the activations.
+    if (upl <= 2) {
+        constexpr int R = 2;
+        const int grid = max(1, min(1792, (N + 4 * R - 1) / (4 * R)));
+        const int rpw = (N + 4 * grid - 1) / (4 * grid);
+        if (upl == 1)
+            hipLaunchKernelGGL((q4k_gemv_kernel<1, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y);
+        else
+            hipLaunchKernelGGL((q4k_gemv_kernel<2, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y);
+        return hipGetLastError();
+    }
     constexpr int R = 1;
     const int want = 1024;
     const int grid = max(1, min(want, (N + 4 * R - 1) / (4 * R)));
     const int rpw = (N + 4 * grid - 1) / (4 * grid);
     switch (upl) {
-        case 1: hipLaunchKernelGGL((q4k_gemv_kernel<1, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
-        case 2: hipLaunchKernelGGL((q4k_gemv_kernel<2, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
         case 3: hipLaunchKernelGGL((q4k_gemv_kernel<3, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
         case 4: hipLaunchKernelGGL((q4k_gemv_kernel<4, R>), dim3(grid), dim3(256), 0, stream, K, N, rpw, b, x, y); break;
         default:
