@@ -448,9 +448,9 @@ hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, flo
     const int upl = (units + 63) / 64;
     // K <= 4096: two rows per pass, and as many workgroups as give every
     // wavefront a single pass (at 4096 x 14336: 1792 workgroups, 149
-    // registers, 10.4-10.6 us against 11.4-11.9 us for one row per pass over
-    // 1024 workgroups in the same runs). Longer rows keep one row per pass:
-    // two would not fit the registers beside the activations.
+    // registers; 10.4-11.8 us against 11.4-11.9 us for one row per pass over
+    // 1024 workgroups, timed side by side). Longer rows keep one row per
+    // pass: two would not fit the registers beside the activations.
     if (upl <= 2) {
         constexpr int R = 2;
         const int grid = max(1, min(1792, (N + 4 * R - 1) / (4 * R)));
