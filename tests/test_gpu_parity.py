@@ -674,9 +674,12 @@ def test_q4k_gemm_workload():
 
 # The M = 1 cases cover 1 to 4 chunks per lane (K up to 8192), a partly
 # filled last chunk pass (K = 2304: 72 of 128 lanes), the long-row kernel
-# (K > 8192), and N = 4099, where the GEMV grid leaves some wavefronts with
-# no rows (they still take part in the workgroup's activation staging).
-@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (1, 768, 70), (1, 2304, 3), (1, 4096, 4099), (1, 6144, 9),
+# (K > 8192), N = 4099, where the GEMV grid leaves some wavefronts with no
+# rows (they still take part in the workgroup's activation staging), and
+# N = 14339 at K = 256, where each wavefront walks 3 rows in two 2-row passes
+# (the second half empty).
+@pytest.mark.parametrize("M,K,N", [(1, 256, 1), (1, 768, 70), (1, 2304, 3), (1, 4096, 4099), (1, 256, 14339),
+                                   (1, 6144, 9),
                                    (1, 8192, 130), (1, 12288, 33), (1, 20480, 5), (3, 512, 63),
                                    (16, 256, 64), (17, 1024, 65), (40, 2048, 130)])
 def test_q4k_ragged(M, K, N):
