@@ -243,7 +243,7 @@ def main():
     if want("small_m"):
         # few-row decode: M rows of decode-like activations against the same cold weight copies
         rows = {}
-        for M in (2, 4, 8, 16, 32):
+        for M in (2, 4, 6, 8, 16, 32):
             xm = torch.from_numpy(synth.gen.activations(wl, M=M)).to(dev)
             xq_m, xs_m, xsum_m = q4.quantize_act(xm, 32)
             y_m = torch.empty((M, wl.N), dtype=torch.float32, device=dev)

@@ -10,7 +10,8 @@
 //
 // Up to 4 rows with 4-bit codes go to the GEMV-shaped kernel in gemv.hip
 // (activation codes of all rows in registers, 8 v_dot4 per row and block),
-// which is faster there; the kernel below covers the rest.
+// and 5 to 8 rows at N >= 4096 to its variant with the activations in LDS,
+// which are faster there; the kernel below covers the rest.
 //
 // A workgroup owns 16 output columns and all M rows, so every weight block is
 // read once for all rows. K is walked in chunks (2048, 1024 or 512 wide, see
@@ -369,6 +370,8 @@ hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, con
     if (M < 1 || M > GEMM_SMALL_MAX_M) return hipErrorInvalidValue;
     if (gemv_rows_fits(M, K, bits))  // up to 4 rows of 4-bit codes: the GEMV-shaped kernel (gemv.hip)
         return launch_gemv_rows(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (gemv_rows_lds_preferred(M, K, N, fmt == 0 ? 32 : bs, bits))  // 5 to 8 rows, wide N: activations in LDS
+        return launch_gemv_rows_lds(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
     if (fmt == 0) {
         if (bits != 4) return hipErrorInvalidValue;
         return launch_fmt<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);

@@ -56,6 +56,25 @@ hipError_t launch_gemv_rows(int M, int K, int N, int bs, int fmt, const uint8_t*
                             const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                             int32_t* partials, hipStream_t stream);
 
+// Few-row GEMV with the activation operands staged in LDS once per workgroup
+// (4-bit codes, M*K codes plus 8 bytes of scale and code sum per (row, block
+// or group) within ROWS_LDS_MAX_BYTES). launch_gemm_small takes it for
+// GEMV_ROWS_MAX_M < M <= GEMV_ROWS_LDS_MAX_M when N fills one workgroup of 16
+// weight rows per CU (measured at K = 4096, Q4_0, N = 4096: 6.4 us at M = 5
+// and 7.7 us at M = 8 against 8.2-8.3 us for the MFMA kernel; N = 14336, M = 8:
+// 20.2 against 27.3 us; at 12 and 16 rows, or N = 1000, the MFMA kernel is
+// faster). Same arguments as launch_gemm.
+constexpr int GEMV_ROWS_LDS_MAX_M = 8;
+constexpr int GEMV_ROWS_LDS_MIN_N = 4096;
+constexpr int ROWS_LDS_MAX_BYTES = 160 * 1024;
+constexpr int ROWS_LDS_GRID = 256;  // workgroups of 16 wavefronts: one per CU
+size_t gemv_rows_lds_bytes(int M, int K, int bs);
+bool gemv_rows_lds_fits(int M, int K, int bs, int bits);
+bool gemv_rows_lds_preferred(int M, int K, int N, int bs, int bits);
+hipError_t launch_gemv_rows_lds(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                                const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
+                                int32_t* partials, hipStream_t stream);
+
 // Packed weights for the tiled GEMM (layout in include/q4.h, q4_pack_weights).
 size_t packed_code_bytes(int K, int N);
 size_t packed_scale_bytes(int K, int N, int bs);

@@ -141,10 +141,13 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
  * [M][K/bs], y [M][N]; affine codes may be 4, 6 or 8 bits (bits; 8-bit codes
  * enter the matrix cores as q - 128 with 128*s folded into the bias term).
  * M*K and N*K*bits/8 must be below 2^31.
- * Three kernels, chosen by M (and the code width):
+ * Four kernels, chosen by M, N, K (and the code width):
  *   M <= 4 with 4-bit codes: the decode GEMV's weight stream, each weight
  *     chunk unpacked once and dotted (v_dot4) with the codes of every row,
  *     which are held in registers.
+ *   5 <= M <= 8 with 4-bit codes, N >= 4096 and M*K*(1 + 8/bs) <= 160 KiB:
+ *     the same weight stream, with the rows' activation codes, scales and
+ *     code sums copied into LDS once per workgroup of 16 wavefronts.
  *   other M <= 32, and 33 <= M <= 64 with N <= 8192: every weight block is
  *     read once for all rows (16x16x32 int8 MFMA on one, two or four 16-row
  *     tiles, 16 output columns per workgroup, K chunks staged in LDS and

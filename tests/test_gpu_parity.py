@@ -327,7 +327,13 @@ SMALL_CASES = [("q4_0", 32, 2, 416, 37), ("q4_0", 32, 16, 96, 17), ("q4_0", 32, 
                # up to 4 rows of 4-bit codes: the GEMV-shaped kernel (several K passes, pass tails,
                # ragged N, and N smaller than a workgroup's rows)
                ("affine", 64, 4, 4160, 45), ("affine", 128, 1, 8320, 19), ("q4_0", 32, 3, 12320, 7),
-               ("affine", 128, 2, 256, 3), ("q4_0", 32, 4, 32, 9)]
+               ("affine", 128, 2, 256, 3), ("q4_0", 32, 4, 32, 9),
+               # 5 to 8 rows at N >= 4096: the GEMV-shaped kernel with the activations in LDS
+               # (a ragged second K pass and two rows per wavefront; half the lanes past K; four
+               # passes of 128-groups with a half-filled last one; the largest K whose codes,
+               # scales and sums fill the 160 KB of LDS)
+               ("q4_0", 32, 5, 4192, 4099), ("affine", 64, 8, 2048, 4096), ("affine", 128, 7, 14336, 4100),
+               ("q4_0", 32, 6, 8192, 4096), ("q4_0", 32, 8, 16384, 4096)]
 
 
 @pytest.mark.parametrize("fmt,bs,M,K,N", SMALL_CASES)
@@ -374,6 +380,24 @@ def test_small_gemm_dispatch_boundary():
         y = q4.gemm("affine", 64, *g, *[to_dev(a[:m]) for a in act])
         _sync()
         assert rel_rms(to_np(y), ref[:m]) <= TOL, m
+
+
+def test_small_gemm_rows_lds_boundary():
+    # at N = 4096: 4 rows take the register GEMV-shaped kernel, 5 and 8 its LDS
+    # variant, 9 the MFMA kernel; K = 16416 at 8 rows needs more LDS than a
+    # workgroup has and goes to the MFMA kernel too. All against the oracle.
+    print("case small rows/lds/mfma boundary M=4,5,8,9", flush=True)
+    wts, act = _partials_case("affine", 128, 9, 1024, 4096, 4343)
+    g = _wts_dev("affine", wts)
+    ref = _oracle_y("affine", wts, act, 1024, 4096, 128)
+    for m in (4, 5, 8, 9):
+        y = q4.gemm("affine", 128, *g, *[to_dev(a[:m]) for a in act])
+        _sync()
+        assert rel_rms(to_np(y), ref[:m]) <= TOL, m
+    wts, act = _partials_case("q4_0", 32, 8, 16416, 4096, 4344)
+    y = q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act])
+    _sync()
+    assert rel_rms(to_np(y), _oracle_y("q4_0", wts, act, 16416, 4096, 32)) <= TOL
 
 
 @pytest.mark.parametrize("fmt,bs,M,N", [("q4_0", 32, 32, 16), ("affine", 64, 17, 20)])
