@@ -81,7 +81,7 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
                                                                  const uint16_t* __restrict__ wbias,
                                                                  const float* __restrict__ dy, float* __restrict__ work) {
     __shared__ BwdLds S[2];  // stage i in S[i & 1]; the next stage's loads wait in registers
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kb = blockIdx.x, nc = blockIdx.y, m0 = blockIdx.z * 16;
     const int nbeg = nc * rows_per, nend = min(N, nbeg + rows_per);
     const int nst = nend > nbeg ? (nend - nbeg + RC - 1) / RC : 0;  // 64-row stages of the range

@@ -306,7 +306,8 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
     constexpr int XCH = 16 * QK / 4 / NTH;  // float4 of the activation tile per thread (16 / W)
     static_assert(XCH * NTH == 16 * QK / 4, "staging covers the tile");
     __shared__ Q4kStage<W, KP> st[KP];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wavefront index is uniform: the K range, and with it every load's scalar offset, stays in SGPRs
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int p = wave / W, tp = tid - p * NTH;  // K range, thread within the range's group
     const int m0 = blockIdx.y * 16;
     const int n = blockIdx.x * (16 * W) + (wave % W) * 16 + (lane & 15);
