@@ -122,11 +122,14 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
         } else {
             o = in ? (uint32_t)((size_t)n * (K / 2) + (size_t)kb * 128 + 32 * part) : OUT;
             const int g0 = (kb * 256 + 32 * s0) / G, g1 = (kb * 256 + 32 * (s0 + 1)) / G;
-            const uint32_t ob = in ? (uint32_t)((size_t)n * ngroups * 2) : OUT;
-            ra0 = __builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g0 * 2, 0);
-            ra1 = __builtin_amdgcn_raw_buffer_load_b16(r_s, ob, g1 * 2, 0);
-            rb0 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g0 * 2, 0) : 0u;
-            rb1 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, ob, g1 * 2, 0) : 0u;
+            // the group offsets differ between lanes: per-lane offsets (a scalar offset
+            // that varies over the wavefront makes the compiler loop over its values)
+            const uint32_t ob = (uint32_t)((size_t)n * ngroups * 2);
+            const uint32_t o0 = in ? ob + 2u * g0 : OUT, o1 = in ? ob + 2u * g1 : OUT;
+            ra0 = __builtin_amdgcn_raw_buffer_load_b16(r_s, o0, 0, 0);
+            ra1 = __builtin_amdgcn_raw_buffer_load_b16(r_s, o1, 0, 0);
+            rb0 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, o0, 0, 0) : 0u;
+            rb1 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, o1, 0, 0) : 0u;
         }
         // Q4_K blocks are 144 bytes: 16-byte aligned offsets (144 = 9 * 16), so 128-bit loads
         rc0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
