@@ -355,7 +355,7 @@ def test_small_gemm_ragged(fmt, bs, M, K, N):
     assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
 
 
-@pytest.mark.parametrize("M", [2, 4, 8, 16, 32, 64])
+@pytest.mark.parametrize("M", [2, 4, 6, 8, 16, 32, 64])
 def test_small_gemm_decode_rows(M):
     # the decode workload's weights against M rows drawn like its activation vector
     print(f"case small gemm q4_0 decode rows M={M}", flush=True)
@@ -488,11 +488,14 @@ def test_bits_gemm_ragged(bits, g, M, K, N):
     assert rel_rms(to_np(y), ref) <= TOL
 
 
-@pytest.mark.parametrize("bits,g", [(6, 64), (8, 64), (8, 128)])
-def test_bits_gemm_workload_sampled(bits, g):
-    # the M=1024, K=N=4096 bf16 workload with its weights quantized at 6 or 8 bits
-    print(f"case gemm {bits}-bit g={g} 1024x4096x4096 sampled", flush=True)
-    wl, x, w16, _, _ = workload_data("affine_g64_1024x4096x4096")
+@pytest.mark.parametrize("bits,g,name", [(6, 64, "affine_g64_1024x4096x4096"), (8, 64, "affine_g64_1024x4096x4096"),
+                                        (8, 128, "affine_g64_1024x4096x4096"),
+                                        (6, 128, "affine_g128_4096x4096x14336"),
+                                        (8, 128, "affine_g128_4096x4096x14336")])
+def test_bits_gemm_workload_sampled(bits, g, name):
+    # a bf16 workload with its weights quantized at 6 or 8 bits (the widths bench.py times)
+    print(f"case gemm {bits}-bit g={g} {name} sampled", flush=True)
+    wl, x, w16, _, _ = workload_data(name)
     wq, ws, wb = oracle.quantize_affine(w16, g, bits)
     gq, gs, gsum = q4.quantize_act(to_dev(x), g)
     y = q4.gemm("affine", g, to_dev(wq), to_dev(ws, torch.bfloat16), to_dev(wb, torch.bfloat16), gq, gs, gsum,
