@@ -569,8 +569,11 @@ def test_gemm_packed_ragged(fmt, bs, M, K, N):
         assert torch.equal(y, yu)
 
 
-@pytest.mark.parametrize("name", ["affine_g128_4096x4096x14336", "affine_g128_4096x14336x4096"])
+@pytest.mark.parametrize("name", ["affine_g128_4096x4096x14336", "affine_g128_4096x14336x4096",
+                                  "affine_g64_1024x4096x4096", "q4_0_minilm_64x384x1536"])
 def test_gemm_packed_workload_sampled(name):
+    # every prefill workload bench.py times on packed weights; above 64 rows q4_gemm
+    # runs the same tiled kernel on the unpacked layout, so the outputs are identical
     print(f"case gemm packed sampled {name}", flush=True)
     wl, x, _, _, wts = workload_data(name)
     g = _wts_dev(wl.fmt, wts)
@@ -581,7 +584,10 @@ def test_gemm_packed_workload_sampled(name):
     yu = q4.gemm(wl.fmt, wl.bs, *g, gq, gs, gsum)
     _sync()
     assert torch.equal(xq, gq) and torch.equal(xs_gm.t(), gs) and torch.equal(xsum_gm.t(), gsum)
-    assert torch.equal(y, yu)
+    if wl.M > 64:
+        assert torch.equal(y, yu)
+    else:  # the few-row kernel sums in another order
+        assert rel_rms(to_np(y), to_np(yu).astype(np.float64)) <= TOL
     act = (to_np(gq), to_np(gs), to_np(gsum))
     ms, ns = sample_pairs(wl.M, wl.N, 1000, wl.K + 7)
     ref = _oracle_y_sample(wl.fmt, wts, act, wl.K, wl.N, wl.bs, ms, ns)
