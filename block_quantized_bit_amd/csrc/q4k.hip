@@ -99,7 +99,9 @@ struct Q4kPass {
 // ((2i + h) * 4 + t) * 64 + l, h = 0 for the low-nibble weights, 1 for the
 // high -- so that each wavefront's register fill is 16-byte reads by
 // consecutive lanes (no bank conflicts), and the vector memory path carries
-// x once per workgroup instead of once per wavefront.
+// x once per workgroup instead of once per wavefront. The per-half sums are
+// formed in the same copy: each copying thread adds its float4, and each lane
+// adds the four partial sums of its half.
 // Every load is a buffer load with no branch around it: the wavefront's buffer
 // range covers only its own rows, and offsets past the end read zero (a zero
 // header makes a row's terms zero). UPL = chunks per lane (K / 2048, rounded up).
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, int rows_pe
                                                        const uint8_t* __restrict__ blocks,
                                                        const float* __restrict__ x, float* __restrict__ y) {
     __shared__ float4 xlds[UPL * 8 * 64];
+    __shared__ float4 slds[UPL * 2 * 64];  // (i, h, l): the sums of the half's four float4, one per t
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = gw * rows_per_wave;
@@ -133,7 +136,12 @@ __global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, int rows_pe
     Q4kPass<UPL, R> cur;
     cur.load(r_w, 0, lane, units, rowbytes, j);
 #pragma unroll
-    for (int m = 0; m < UPL * 2; ++m) xlds[(int)threadIdx.x + 256 * m] = xv[m];
+    for (int m = 0; m < UPL * 2; ++m) {
+        const int e = (int)threadIdx.x + 256 * m;  // ((2i + h) * 4 + t) * 64 + l
+        xlds[e] = xv[m];
+        reinterpret_cast<float*>(slds)[((e >> 8) * 64 + (e & 63)) * 4 + ((e >> 6) & 3)] =
+            (xv[m].x + xv[m].y) + (xv[m].z + xv[m].w);
+    }
     __syncthreads();
     if (nrows == 0) return;
 
@@ -147,12 +155,9 @@ __global__ __launch_bounds__(256) void q4k_gemv_kernel(int K, int N, int rows_pe
             xl[i][4 * t] = a.x; xl[i][4 * t + 1] = a.y; xl[i][4 * t + 2] = a.z; xl[i][4 * t + 3] = a.w;
             xh[i][4 * t] = b.x; xh[i][4 * t + 1] = b.y; xh[i][4 * t + 2] = b.z; xh[i][4 * t + 3] = b.w;
         }
-        sl[i] = sh[i] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            sl[i] += xl[i][t];
-            sh[i] += xh[i][t];
-        }
+        const float4 pl = slds[(2 * i) * 64 + lane], ph = slds[(2 * i + 1) * 64 + lane];
+        sl[i] = (pl.x + pl.y) + (pl.z + pl.w);
+        sh[i] = (ph.x + ph.y) + (ph.z + ph.w);
     }
 
     for (int p = 0; p < nrows; p += R) {
