@@ -676,20 +676,25 @@ def test_q4k_gemm_row_magnitudes():
     # halves, with a power-of-two scale per row and super-block: rows far
     # outside the f16 range (1e20, 1e-20, 1e-33), near its top (3e4), and a row
     # whose super-blocks differ by 1e12 must each match the oracle on their own.
+    # A row of zeros (its largest magnitude, taken over the bit patterns, is 0 and
+    # the scale exponent is clamped) must give exact zeros, and a row whose first
+    # super-block is zero must match the oracle.
     print("case q4k gemm row magnitudes", flush=True)
     K, N = 768, 70
     rng = np.random.default_rng(4321)
     w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
     blocks = oracle.quantize_q4k(w)
-    scales = np.array([1e-20, 1e-5, 1.0, 3e4, 1e5, 1e20, 7.0, 1e-33], dtype=np.float64)
-    x = (rng.standard_normal((8, K)) * scales[:, None]).astype(np.float32)
+    scales = np.array([1e-20, 1e-5, 1.0, 3e4, 1e5, 1e20, 7.0, 1e-33, 0.0, 1.0], dtype=np.float64)
+    x = (rng.standard_normal((10, K)) * scales[:, None]).astype(np.float32)
     x[6, 256:512] *= np.float32(1e12)   # super-block 1 of row 6: 1e12 x the others
+    x[9, 0:256] = 0.0                   # super-block 0 of row 9: zeros
     ref = oracle.q4k_gemm(blocks, x, K, N)
     y = q4.q4k_gemm(to_dev(blocks), to_dev(x), N)
     _sync()
     got = to_np(y)
     assert np.all(np.isfinite(got))
-    for m in range(8):
+    assert np.all(got[8] == 0.0) and np.all(ref[8] == 0.0)
+    for m in (0, 1, 2, 3, 4, 5, 6, 7, 9):
         assert rel_rms(got[m], ref[m]) <= TOL, m
 
 
