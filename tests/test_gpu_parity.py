@@ -382,6 +382,31 @@ def test_small_gemm_dispatch_boundary():
         assert rel_rms(to_np(y), ref[:m]) <= TOL, m
 
 
+@pytest.mark.parametrize("M", [3, 6, 16, 100])
+def test_gemm_activation_row_extremes(M):
+    # An all-zero activation row (scale 0, codes 0) must give exact zeros, and
+    # rows scaled by 1e-30 and 1e30 must match the oracle, on every q4_gemm path
+    # at N = 4096: 3 rows take the register GEMV-shaped kernel, 6 its LDS
+    # variant, 16 the MFMA few-row kernel and 100 the tiled kernel.
+    print(f"case gemm activation row extremes M={M}", flush=True)
+    K, N = 512, 4096
+    rng = np.random.default_rng(9000 + M)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[0] = 0.0
+    x[1] *= np.float32(1e-30)
+    x[2] *= np.float32(1e30)
+    act = oracle.quantize_act(x, 32)
+    wts = oracle.quantize_q4_0((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    y = q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act])
+    _sync()
+    got = to_np(y)
+    ref = _oracle_y("q4_0", wts, act, K, N, 32)
+    assert np.all(np.isfinite(got))
+    assert np.all(got[0] == 0.0)
+    for m in range(1, M):
+        assert rel_rms(got[m], ref[m]) <= TOL, m
+
+
 def test_small_gemm_rows_lds_boundary():
     # at N = 4096: 4 rows take the register GEMV-shaped kernel, 5 and 8 its LDS
     # variant, 9 the MFMA kernel; K = 16416 at 8 rows needs more LDS than a
