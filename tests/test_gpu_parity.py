@@ -861,6 +861,40 @@ def test_gemv_fused_long_k(fmt, bs, xdt, K, N):
     assert rel_rms(to_np(y), _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
 
 
+@pytest.mark.parametrize("fmt,bs", [("q4_0", 32), ("affine", 64), ("affine", 128)])
+def test_gemv_fused_activation_extremes(fmt, bs):
+    # the quantization inside the decode kernel at its edges: blocks of zeros
+    # (scale 0, codes 0), blocks scaled by 1e-30 and 1e30, one huge entry in a
+    # block; then an all-zero vector, whose output must be exact zeros
+    print(f"case gemv_fused activation extremes {fmt} bs={bs}", flush=True)
+    K, N = 4096, 300
+    rng = np.random.default_rng(bs + 17)
+    x = rng.standard_normal((1, K)).astype(np.float32)
+    x[0, 0:bs] = 0.0
+    x[0, bs:2 * bs] *= np.float32(1e-30)
+    x[0, 2 * bs:3 * bs] *= np.float32(1e30)
+    x[0, 3 * bs + 5] = np.float32(3e35)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    wts = oracle.quantize_q4_0(w) if fmt == "q4_0" else oracle.quantize_affine(synth.bf16_bits(w), bs)
+    g = _wts_dev(fmt, wts)
+    for xv in (x, np.zeros_like(x)):
+        act = oracle.quantize_act(xv, bs)
+        gx = to_dev(xv)
+        out = (torch.empty((1, K), dtype=torch.int8, device=gx.device),
+               torch.empty((1, K // bs), dtype=torch.float32, device=gx.device),
+               torch.empty((1, K // bs), dtype=torch.int32, device=gx.device))
+        y = q4.gemv_fused(fmt, bs, gx, *g, act_out=out)
+        _sync()
+        for a, b in zip(out, act):
+            assert np.array_equal(to_np(a).view(np.uint8), b.view(np.uint8))
+        got = to_np(y)
+        assert np.all(np.isfinite(got))
+        if not xv.any():
+            assert np.all(got == 0.0)
+        else:
+            assert rel_rms(got, _oracle_y(fmt, wts, act, K, N, bs)) <= TOL
+
+
 def test_gemv_fused_near_ties_and_ragged():
     print("case gemv_fused near ties, ragged N", flush=True)
     x = _near_tie_activations(1, 8192, 32, 5)
