@@ -910,3 +910,34 @@ def test_gemv_fused_near_ties_and_ragged():
     for a, b in zip(out, act):
         assert np.array_equal(to_np(a).view(np.uint8), b.view(np.uint8))
     assert rel_rms(to_np(y), _oracle_y("q4_0", wts, act, 8192, 77, 32)) <= TOL
+
+
+@pytest.mark.parametrize("bs,nblocks,seed", [(32, 24, 1), (64, 8, 2), (128, 4, 3)])
+def test_quantize_act_exact_reading(bs, nblocks, seed):
+    # the near-tie blocks of the oracle's exact pins, checked against exact
+    # rational arithmetic directly (not only against the oracle): the
+    # standalone quantizer and the fused decode GEMV's codes
+    from tests.test_oracle_act import check_exact_codes
+    print(f"case exact activation codes bs={bs}", flush=True)
+
+    def standalone(x, bs):
+        got = q4.quantize_act(to_dev(x), bs)
+        _sync()
+        return [to_np(t) for t in got]
+
+    def fused(x, bs):
+        K = x.shape[1]
+        fmt = "q4_0" if bs == 32 else "affine"
+        rng = np.random.default_rng(bs)
+        w = (0.02 * rng.standard_normal((40, K))).astype(np.float32)
+        wts = oracle.quantize_q4_0(w) if fmt == "q4_0" else oracle.quantize_affine(synth.bf16_bits(w), bs)
+        gx = to_dev(x)
+        out = (torch.empty((1, K), dtype=torch.int8, device=gx.device),
+               torch.empty((1, K // bs), dtype=torch.float32, device=gx.device),
+               torch.empty((1, K // bs), dtype=torch.int32, device=gx.device))
+        q4.gemv_fused(fmt, bs, gx, *_wts_dev(fmt, wts), act_out=out)
+        _sync()
+        return [to_np(t) for t in out]
+
+    assert check_exact_codes(standalone, bs, nblocks, seed) == []
+    assert check_exact_codes(fused, bs, nblocks, seed) == []
