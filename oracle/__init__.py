@@ -22,16 +22,30 @@ FMT_AFFINE = 1
 Q4K_BLOCK_BYTES = 144
 Q4K_QK = 256
 
-CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math"]
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-pthread"]
+# The sanitizer build of the same source (host code only; run by the CPU tests
+# with the sanitizer runtimes preloaded into the Python process).
+SAN_CFLAGS = ["-O1", "-g", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-pthread",
+              "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+# ORACLE_LIB names a prebuilt oracle library to load instead (the sanitizer build).
+_ENV_LIB = os.environ.get("ORACLE_LIB")
 
 
 def build(force: bool = True) -> str:
     """Compile oracle.c with plain gcc (no -ffast-math, no -march=native)."""
+    if _ENV_LIB:
+        return _ENV_LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer into `path`."""
+    subprocess.check_call(["gcc", *SAN_CFLAGS, _SRC, "-o", path, "-lm"])
+    return path
 
 
 _lib = None
@@ -41,9 +55,11 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         build(force=False)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(_ENV_LIB or _LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
+        L.or_set_threads.argtypes = [I]
+        L.or_set_threads.restype = I
         L.or_f16_to_f32.restype = ctypes.c_float
         L.or_f16_to_f32.argtypes = [ctypes.c_uint16]
         L.or_f32_to_f16.restype = ctypes.c_uint16
@@ -84,6 +100,12 @@ def lib() -> ctypes.CDLL:
         L.or_q4_backward_sample.argtypes = [I, I, I, I, I, P, P, P, P, I, P, P, P]
         _lib = L
     return _lib
+
+
+def set_threads(t: int) -> int:
+    """Threads the products (q4_gemm, q4k_gemv, q4k_gemm) split their output
+    columns over; results are bit-identical for every count. Returns the count set."""
+    return lib().or_set_threads(int(t))
 
 
 def _p(a: np.ndarray):

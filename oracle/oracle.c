@@ -52,12 +52,66 @@
  *     bits [6f, 6f + 6) of the 96-bit string.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define OR_OK 0
 #define OR_BAD 1
+
+/* ------------------------------------------------------------------------ */
+/* Threads (used only to time the oracle on a host's cores)                  */
+/* ------------------------------------------------------------------------ */
+
+/* The products below can split their output columns n over T threads: a
+ * static partition into T contiguous ranges, each output computed by exactly
+ * one thread with the same arithmetic in the same order as with one thread,
+ * so the results are bit-identical for every T (C-Kernel-Engine's kernel
+ * rules keep threading out of the kernels; here it sits outside the
+ * per-output arithmetic). */
+#define OR_MAX_THREADS 256
+static int g_threads = 1;
+
+int or_set_threads(int t) {
+    g_threads = t < 1 ? 1 : (t > OR_MAX_THREADS ? OR_MAX_THREADS : t);
+    return g_threads;
+}
+
+struct or_range { void (*fn)(const void*, long, long); const void* ctx; long n0, n1; };
+
+static void* or_range_main(void* p) {
+    const struct or_range* r = (const struct or_range*)p;
+    r->fn(r->ctx, r->n0, r->n1);
+    return NULL;
+}
+
+/* fn(ctx, n0, n1) over a partition of [0, n). Returns OR_BAD if a thread
+ * could not be started (the work done so far is then incomplete). */
+static int for_ranges(long n, void (*fn)(const void*, long, long), const void* ctx) {
+    long T = g_threads < n ? g_threads : n;
+    if (T <= 1) {
+        fn(ctx, 0, n);
+        return OR_OK;
+    }
+    pthread_t th[OR_MAX_THREADS];
+    struct or_range r[OR_MAX_THREADS];
+    long started = 0;
+    int rc = OR_OK;
+    for (long t = 0; t < T; ++t) {
+        r[t].fn = fn;
+        r[t].ctx = ctx;
+        r[t].n0 = n * t / T;
+        r[t].n1 = n * (t + 1) / T;
+        if (pthread_create(&th[t], NULL, or_range_main, &r[t]) != 0) {
+            rc = OR_BAD;
+            break;
+        }
+        ++started;
+    }
+    for (long t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    return rc;
+}
 
 /* ------------------------------------------------------------------------ */
 /* Number formats (IEEE 754 binary16 and bfloat16)                           */
@@ -384,15 +438,27 @@ static float one_output(int N, int K, int bs, int fmt, int bits, const uint8_t* 
     return (float)y;
 }
 
+struct gemm_ctx {
+    int M, K, N, bs, fmt, bits;
+    const uint8_t* wq; const uint16_t* ws; const uint16_t* wb;
+    const int8_t* xq; const float* xs; const int32_t* xsum; float* y;
+};
+
+static void gemm_cols(const void* p, long n0, long n1) {
+    const struct gemm_ctx* c = (const struct gemm_ctx*)p;
+    for (long m = 0; m < c->M; ++m)
+        for (long n = n0; n < n1; ++n)
+            c->y[m * (long)c->N + n] =
+                one_output(c->N, c->K, c->bs, c->fmt, c->bits, c->wq, c->ws, c->wb, c->xq, c->xs, c->xsum, m, n);
+}
+
 /* y [M][N] float32. */
 int or_q4_gemm_bits(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq,
                     const uint16_t* wscale, const uint16_t* wbias, const int8_t* xq,
                     const float* xs, const int32_t* xsum, float* y) {
     if (check_fmt_bits(K, bs, fmt, bits) || M < 0 || N < 0) return OR_BAD;
-    for (long m = 0; m < M; ++m)
-        for (long n = 0; n < N; ++n)
-            y[m * (long)N + n] = one_output(N, K, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, m, n);
-    return OR_OK;
+    struct gemm_ctx c = {M, K, N, bs, fmt, bits, wq, wscale, wbias, xq, xs, xsum, y};
+    return for_ranges(N, gemm_cols, &c);
 }
 
 int or_q4_gemm(int M, int K, int N, int bs, int fmt, const uint8_t* wq,
@@ -562,17 +628,24 @@ static float q4k_one(int K, const uint8_t* blocks, const float* x, long m, long 
 
 /* [cke] gemm_q4_k_ref: the GEMM is one GEMV per activation row.
  * x [M][K] float32, blocks [N][K/256] x 144 B, y [M][N]. */
+struct q4k_gemm_ctx { int M, K, N; const uint8_t* blocks; const float* x; float* y; };
+
+static void q4k_cols(const void* p, long n0, long n1) {
+    const struct q4k_gemm_ctx* c = (const struct q4k_gemm_ctx*)p;
+    for (long m = 0; m < c->M; ++m)
+        for (long n = n0; n < n1; ++n) c->y[m * (long)c->N + n] = q4k_one(c->K, c->blocks, c->x, m, n);
+}
+
 int or_q4k_gemv(int K, int N, const uint8_t* blocks, const float* x, float* y) {
     if (K <= 0 || K % QK != 0 || N < 0) return OR_BAD;
-    for (long n = 0; n < N; ++n) y[n] = q4k_one(K, blocks, x, 0, n);
-    return OR_OK;
+    struct q4k_gemm_ctx c = {1, K, N, blocks, x, y};
+    return for_ranges(N, q4k_cols, &c);
 }
 
 int or_q4k_gemm(int M, int K, int N, const uint8_t* blocks, const float* x, float* y) {
     if (M < 0 || K <= 0 || K % QK != 0 || N < 0) return OR_BAD;
-    for (long m = 0; m < M; ++m)
-        if (or_q4k_gemv(K, N, blocks, x + m * (long)K, y + m * (long)N)) return OR_BAD;
-    return OR_OK;
+    struct q4k_gemm_ctx c = {M, K, N, blocks, x, y};
+    return for_ranges(N, q4k_cols, &c);
 }
 
 int or_q4k_gemm_sample(int M, int K, int N, const uint8_t* blocks, const float* x,
