@@ -24,7 +24,7 @@ Q4K_BLOCK_BYTES = 144
 EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
            "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string", "q4_packed_bytes", "q4_pack_weights",
            "q4_gemm_packed_work_bytes", "q4_gemm_packed", "q4_backward_work_bytes", "q4k_gemm_backward",
-           "q4_gemm_backward")
+           "q4_gemm_backward", "q4_measure_empty", "q4_measure_stream_read")
 _SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes", "q4_backward_work_bytes")
 
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.q4_backward_work_bytes.argtypes = [I, I, I]
         L.q4k_gemm_backward.argtypes = [I, I, I, P, P, P, P, P]
         L.q4_gemm_backward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+        L.q4_measure_empty.argtypes = [I, I, P]
+        L.q4_measure_stream_read.argtypes = [P, ctypes.c_size_t, I, I, ctypes.c_uint32, P, P]
         for name in EXPORTS:
             if name in _SIZE_T_FUNCS:
                 getattr(L, name).restype = ctypes.c_size_t
@@ -305,3 +307,19 @@ def q4k_quantize_weights(w: torch.Tensor, stream=None):
     blocks = torch.empty((N, K // 256 * Q4K_BLOCK_BYTES), dtype=torch.uint8, device=w.device)
     _check(lib().q4k_quantize_weights(N, K, _ptr(w), _ptr(blocks), _stream(stream)), "q4k_quantize_weights")
     return blocks
+
+
+# ---- measurement kernels (include/q4_measure.h) ------------------------------------
+
+def measure_empty(grid: int, block: int, stream=None):
+    """One empty kernel of the given launch shape (the dispatch floor)."""
+    _check(lib().q4_measure_empty(grid, block, _stream(stream)), "q4_measure_empty")
+
+
+def measure_stream_read(buf: torch.Tensor, grid: int, block: int, sink: torch.Tensor, key: int = 0x9E3779B9,
+                        stream=None):
+    """Read every byte of buf once (128-bit non-temporal loads); sink (one int32) is written only if the XOR of
+    the data equals key."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().q4_measure_stream_read(_ptr(buf), nbytes, grid, block, key, _ptr(sink), _stream(stream)),
+           "q4_measure_stream_read")

@@ -22,14 +22,18 @@ MIS = 0x100001
 
 
 def declared_functions():
-    text = open(os.path.join(ROOT, "include", "q4.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(q4k?_\w+)\(", text, flags=re.M)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(q4k?_\w+)\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None
