@@ -24,7 +24,7 @@ Q4K_BLOCK_BYTES = 144
 EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
            "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string", "q4_packed_bytes", "q4_pack_weights",
            "q4_gemm_packed_work_bytes", "q4_gemm_packed", "q4_backward_work_bytes", "q4k_gemm_backward",
-           "q4_gemm_backward", "q4_measure_empty", "q4_measure_stream_read")
+           "q4_gemm_backward", "q4_measure_empty", "q4_measure_stream_read", "q4_debug_partials_fused")
 _SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes", "q4_backward_work_bytes")
 
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.q4_backward_work_bytes.argtypes = [I, I, I]
         L.q4k_gemm_backward.argtypes = [I, I, I, P, P, P, P, P]
         L.q4_gemm_backward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+        L.q4_debug_partials_fused.argtypes = [I, I, I, I, I, I, P, P, P, P]
         L.q4_measure_empty.argtypes = [I, I, P]
         L.q4_measure_stream_read.argtypes = [P, ctypes.c_size_t, I, I, ctypes.c_uint32, P, P]
         for name in EXPORTS:
@@ -190,6 +191,17 @@ def debug_partials(path: str, fmt: str, bs: int, wq, xq, xsum, m0: int = 0, m1: 
     p = {"gemv": Q4_PATH_GEMV, "gemm": Q4_PATH_GEMM, "small": Q4_PATH_SMALL}[path]
     _check(lib().q4_debug_partials(p, M, K, N, bs, _fmt(fmt), bits, _ptr(wq), _ptr(xq), _ptr(xsum), m0, m1,
                                    _ptr(out), _stream(stream)), "q4_debug_partials")
+    return out
+
+
+def debug_partials_fused(fmt: str, bs: int, x, wq, out=None, bits: int = 4, stream=None):
+    """Exact per-block int32 partials [N][K/bs] of the fused decode kernel (it quantizes x [1][K] itself)."""
+    K = x.shape[1]
+    N = wq.numel() * 8 // (K * bits)
+    if out is None:
+        out = torch.empty((N, K // bs), dtype=torch.int32, device=wq.device)
+    _check(lib().q4_debug_partials_fused(K, N, bs, _fmt(fmt), bits, _xdtype(x), _ptr(x), _ptr(wq), _ptr(out),
+                                         _stream(stream)), "q4_debug_partials_fused")
     return out
 
 

@@ -168,6 +168,18 @@ int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits, 
                                       nullptr, partials, s));
 }
 
+int q4_debug_partials_fused(int K, int N, int bs, int fmt, int bits, int xdtype, const void* x, const uint8_t* wq,
+                            int32_t* partials, void* stream) {
+    int st = matmul_status(1, K, N, bs, fmt, bits);
+    if (st) return st;
+    if (xdtype != Q4_DT_F32 && xdtype != Q4_DT_BF16) return Q4_ERR_FORMAT;
+    if (K > Q4_GEMV_MAX_K) return Q4_ERR_DIM;
+    if (!x || !wq || !partials) return Q4_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(partials, 4)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_gemv_fused_partials(K, N, bs, fmt, xdtype == Q4_DT_BF16, x, wq, partials,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t q4_packed_bytes(int K, int N, int bs, int fmt) {
     if (packed_status(K, N, bs, fmt)) return 0;
     return q4::packed_code_bytes(K, N) + q4::packed_scale_bytes(K, N, bs) * (fmt == Q4_FMT_AFFINE ? 2 : 1);

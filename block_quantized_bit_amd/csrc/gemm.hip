@@ -334,10 +334,11 @@ __global__ __launch_bounds__(NT * KSP, KSP == 1 ? 2 : 1) void gemm_kernel(int M,
         return __builtin_bit_cast(v4i, base[swz(row, gi * (G / 16) + 2 * s + half)]);
     };
 
-    // Start value of every MFMA chain: the bits of 1.5 * 2^23, or zero for the
-    // partials and 8-bit codes (the empty asm keeps the 16 registers live
-    // instead of rebuilding them before each chain).
-    constexpr bool BIASED = !PARTIALS && BITS != 8;
+    // Start value of every MFMA chain: the bits of 1.5 * 2^23, or zero for
+    // 8-bit codes (the empty asm keeps the 16 registers live instead of
+    // rebuilding them before each chain). The partials view runs the same
+    // chain and reports its integer minus the start value.
+    constexpr bool BIASED = BITS != 8;
     v16i chain0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) chain0[r] = BIASED ? CHAIN_BIAS : 0;
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(NT * KSP, KSP == 1 ? 2 : 1) void gemm_kernel(int M,
                 if (mb + dr < M && n < N && g < ngroups) {
                     // 8 bits: the MFMA summed (q - 128) * xq; the reported partial is sum q * xq
                     const int fix = BITS == 8 ? 128 * sb[dr * sstride] : 0;
-                    pb[dr * rstride] = d[r] + fix;
+                    pb[dr * rstride] = (d[r] - (BIASED ? CHAIN_BIAS : 0)) + fix;
                 }
             }
             return;

@@ -29,9 +29,6 @@
 // per dword with no byte shuffles; eight v_dot4_i32_i8 give the block's
 // integer dot. Float partial sums are reduced across the wavefront with DPP
 // row operations and lane reads.
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -636,30 +633,12 @@ __global__ __launch_bounds__(64 * ROWS_LDS_WAVES) void gemv_rows_lds_kernel(
     }
 }
 
-// Launch shape: (rows per wave, waves per workgroup, activations in LDS).
-struct GemvShape {
-    int r, waves, lds;
-};
-
-GemvShape gemv_shape(bool fused) {
-    static int cfg[2][3] = {{-1, -1, -1}, {-1, -1, -1}};
-    int* c = cfg[fused ? 1 : 0];
-    if (c[0] < 0) {
-        // defaults; the environment variables are tuning knobs only
-        c[0] = 1;
-        c[1] = fused ? 16 : 8;
-        c[2] = fused ? 1 : 0;
-        const char* e = getenv(fused ? "Q4_GEMV_FUSED_SHAPE" : "Q4_GEMV_SHAPE");  // "R,WAVES,LDS"
-        int r, w, l;
-        if (e && sscanf(e, "%d,%d,%d", &r, &w, &l) == 3 && (r == 1 || r == 2 || r == 4) &&
-            (w == 4 || w == 8 || w == 16)) {
-            c[0] = r;
-            c[1] = w;
-            c[2] = fused ? 1 : (l != 0);
-        }
-    }
-    return GemvShape{c[0], c[1], c[2]};
-}
+// Launch shapes. Plain GEMV (codes given): one row per wavefront, 8 wavefronts
+// per workgroup, codes read from global memory. Fused: one row per wavefront,
+// 16 wavefronts per workgroup sharing the quantization of x into LDS. The
+// partials views run these same shapes with the partials store switched on.
+constexpr int PLAIN_WAVES = 8;
+constexpr int FUSED_WAVES = 16;
 
 template <int FMT, int G, int R, int WAVES, bool FUSED, bool LDS_ACT, bool XBF16, bool PARTIALS>
 hipError_t launch_one(int K, int N, const uint8_t* wq, const void* wscale, const void* wbias, const void* x,
@@ -673,60 +652,27 @@ hipError_t launch_one(int K, int N, const uint8_t* wq, const void* wscale, const
     return hipGetLastError();
 }
 
-template <int FMT, int G, int WAVES, bool FUSED, bool LDS_ACT, bool XBF16, bool PARTIALS>
-hipError_t launch_r(int r, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias, const void* x,
-                    const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
-                    int8_t* xq_out, float* xs_out, int32_t* xsum_out, hipStream_t stream) {
-    if (r == 2)
-        return launch_one<FMT, G, 2, WAVES, FUSED, LDS_ACT, XBF16, PARTIALS>(K, N, wq, wscale, wbias, x, xq, xs, xsum,
-                                                                            y, partials, xq_out, xs_out, xsum_out,
-                                                                            stream);
-    if (r == 4)
-        return launch_one<FMT, G, 4, WAVES, FUSED, LDS_ACT, XBF16, PARTIALS>(K, N, wq, wscale, wbias, x, xq, xs, xsum,
-                                                                            y, partials, xq_out, xs_out, xsum_out,
-                                                                            stream);
-    return launch_one<FMT, G, 1, WAVES, FUSED, LDS_ACT, XBF16, PARTIALS>(K, N, wq, wscale, wbias, x, xq, xs, xsum, y,
-                                                                        partials, xq_out, xs_out, xsum_out, stream);
-}
-
-template <int FMT, int G, bool FUSED, bool LDS_ACT, bool XBF16, bool PARTIALS>
-hipError_t launch_w(GemvShape sh, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
-                    const void* x, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
-                    int32_t* partials, int8_t* xq_out, float* xs_out, int32_t* xsum_out, hipStream_t stream) {
-    if (sh.waves == 8)
-        return launch_r<FMT, G, 8, FUSED, LDS_ACT, XBF16, PARTIALS>(sh.r, K, N, wq, wscale, wbias, x, xq, xs, xsum, y,
-                                                                   partials, xq_out, xs_out, xsum_out, stream);
-    if (sh.waves == 16)
-        return launch_r<FMT, G, 16, FUSED, LDS_ACT, XBF16, PARTIALS>(sh.r, K, N, wq, wscale, wbias, x, xq, xs, xsum,
-                                                                    y, partials, xq_out, xs_out, xsum_out, stream);
-    return launch_r<FMT, G, 4, FUSED, LDS_ACT, XBF16, PARTIALS>(sh.r, K, N, wq, wscale, wbias, x, xq, xs, xsum, y,
-                                                               partials, xq_out, xs_out, xsum_out, stream);
-}
-
 template <int FMT, int G>
 hipError_t launch_fmt(int K, int N, const uint8_t* wq, const void* wscale, const void* wbias, const int8_t* xq,
                       const float* xs, const int32_t* xsum, float* y, int32_t* partials, hipStream_t stream) {
-    const GemvShape sh = gemv_shape(false);
-    if (partials)  // the partials view reads the codes straight from global memory
-        return launch_r<FMT, G, 4, false, false, false, true>(1, K, N, wq, wscale, wbias, nullptr, xq, xs, xsum, y,
-                                                             partials, nullptr, nullptr, nullptr, stream);
-    if (sh.lds)
-        return launch_w<FMT, G, false, true, false, false>(sh, K, N, wq, wscale, wbias, nullptr, xq, xs, xsum, y,
-                                                          nullptr, nullptr, nullptr, nullptr, stream);
-    return launch_w<FMT, G, false, false, false, false>(sh, K, N, wq, wscale, wbias, nullptr, xq, xs, xsum, y,
-                                                       nullptr, nullptr, nullptr, nullptr, stream);
+    if (partials)
+        return launch_one<FMT, G, 1, PLAIN_WAVES, false, false, false, true>(K, N, wq, wscale, wbias, nullptr, xq, xs,
+                                                                            xsum, y, partials, nullptr, nullptr,
+                                                                            nullptr, stream);
+    return launch_one<FMT, G, 1, PLAIN_WAVES, false, false, false, false>(K, N, wq, wscale, wbias, nullptr, xq, xs,
+                                                                         xsum, y, nullptr, nullptr, nullptr, nullptr,
+                                                                         stream);
 }
 
-template <int FMT, int G>
+template <int FMT, int G, bool PARTIALS>
 hipError_t launch_fused_fmt(int K, int N, bool xbf16, const void* x, const uint8_t* wq, const void* wscale,
-                            const void* wbias, float* y, int8_t* xq_out, float* xs_out, int32_t* xsum_out,
-                            hipStream_t stream) {
-    const GemvShape sh = gemv_shape(true);
+                            const void* wbias, float* y, int32_t* partials, int8_t* xq_out, float* xs_out,
+                            int32_t* xsum_out, hipStream_t stream) {
     if (xbf16)
-        return launch_w<FMT, G, true, true, true, false>(sh, K, N, wq, wscale, wbias, x, nullptr, nullptr, nullptr, y,
-                                                        nullptr, xq_out, xs_out, xsum_out, stream);
-    return launch_w<FMT, G, true, true, false, false>(sh, K, N, wq, wscale, wbias, x, nullptr, nullptr, nullptr, y,
-                                                     nullptr, xq_out, xs_out, xsum_out, stream);
+        return launch_one<FMT, G, 1, FUSED_WAVES, true, true, true, PARTIALS>(
+            K, N, wq, wscale, wbias, x, nullptr, nullptr, nullptr, y, partials, xq_out, xs_out, xsum_out, stream);
+    return launch_one<FMT, G, 1, FUSED_WAVES, true, true, false, PARTIALS>(
+        K, N, wq, wscale, wbias, x, nullptr, nullptr, nullptr, y, partials, xq_out, xs_out, xsum_out, stream);
 }
 
 }  // namespace
@@ -744,11 +690,28 @@ hipError_t launch_gemv_fused(int K, int N, int bs, int fmt, bool xbf16, const vo
                              const void* wscale, const void* wbias, float* y, int8_t* xq_out, float* xs_out,
                              int32_t* xsum_out, hipStream_t stream) {
     if (fmt == 0)
-        return launch_fused_fmt<0, 32>(K, N, xbf16, x, wq, wscale, wbias, y, xq_out, xs_out, xsum_out, stream);
+        return launch_fused_fmt<0, 32, false>(K, N, xbf16, x, wq, wscale, wbias, y, nullptr, xq_out, xs_out,
+                                              xsum_out, stream);
     if (bs == 64)
-        return launch_fused_fmt<1, 64>(K, N, xbf16, x, wq, wscale, wbias, y, xq_out, xs_out, xsum_out, stream);
+        return launch_fused_fmt<1, 64, false>(K, N, xbf16, x, wq, wscale, wbias, y, nullptr, xq_out, xs_out,
+                                              xsum_out, stream);
     if (bs == 128)
-        return launch_fused_fmt<1, 128>(K, N, xbf16, x, wq, wscale, wbias, y, xq_out, xs_out, xsum_out, stream);
+        return launch_fused_fmt<1, 128, false>(K, N, xbf16, x, wq, wscale, wbias, y, nullptr, xq_out, xs_out,
+                                               xsum_out, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv_fused_partials(int K, int N, int bs, int fmt, bool xbf16, const void* x, const uint8_t* wq,
+                                      int32_t* partials, hipStream_t stream) {
+    if (fmt == 0)
+        return launch_fused_fmt<0, 32, true>(K, N, xbf16, x, wq, nullptr, nullptr, nullptr, partials, nullptr,
+                                             nullptr, nullptr, stream);
+    if (bs == 64)
+        return launch_fused_fmt<1, 64, true>(K, N, xbf16, x, wq, nullptr, nullptr, nullptr, partials, nullptr,
+                                             nullptr, nullptr, stream);
+    if (bs == 128)
+        return launch_fused_fmt<1, 128, true>(K, N, xbf16, x, wq, nullptr, nullptr, nullptr, partials, nullptr,
+                                              nullptr, nullptr, stream);
     return hipErrorInvalidValue;
 }
 

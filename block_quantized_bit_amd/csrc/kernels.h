@@ -24,6 +24,10 @@ hipError_t launch_gemv(int K, int N, int bs, int fmt, const uint8_t* wq, const v
 hipError_t launch_gemv_fused(int K, int N, int bs, int fmt, bool xbf16, const void* x, const uint8_t* wq,
                              const void* wscale, const void* wbias, float* y, int8_t* xq_out, float* xs_out,
                              int32_t* xsum_out, hipStream_t stream);
+// The same fused kernel with the integer-partials store in place of the float
+// epilogue (partials [N][K/bs], from the codes the kernel quantizes itself).
+hipError_t launch_gemv_fused_partials(int K, int N, int bs, int fmt, bool xbf16, const void* x, const uint8_t* wq,
+                                      int32_t* partials, hipStream_t stream);
 
 // bits: code width of affine weights (4, 6 or 8; Q4_0 is 4-bit only).
 hipError_t launch_gemm(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq, const void* wscale,

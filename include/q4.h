@@ -59,6 +59,11 @@
  *   64c + l is the low nibble of qs[32c + l] (sub-block 2c), weight
  *   64c + 32 + l its high nibble (sub-block 2c+1). Weight value
  *   d * sc[s] * q - dmin * m[s].
+ *   The packing of the sixteen 6-bit fields is this library's own (the
+ *   C-Kernel-Engine page calls an unpack routine whose body it does not
+ *   show). llama.cpp-style Q4_K blocks store the high bits of the scales and
+ *   mins of sub-blocks 4..7 differently, so such blocks cannot be exchanged
+ *   with these: repack them with q4k_quantize_weights from float weights.
  */
 #ifndef Q4_H
 #define Q4_H
@@ -171,8 +176,11 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
  * (path Q4_PATH_GEMV, needs M == 1) or q4_gemm (Q4_PATH_GEMM: the tiled
  * kernel, any row count; Q4_PATH_SMALL: the few-row kernels, which q4_gemm
  * takes as described there, for m1 - m0 <= 64 rows at any N, else
- * Q4_ERR_RANGE): the same kernels, compiled
- * with the partials store in place of the float epilogue.
+ * Q4_ERR_RANGE): the same kernels at the same launch shapes, compiled with
+ * the partials store in place of the float epilogue. The tiled kernel's
+ * integer chains start from the same exponent bias as in q4_gemm (the bits
+ * of 1.5 * 2^23 for 4- and 6-bit codes) and report the chain's integer minus
+ * that start value.
  * partials [(m1-m0)][N][K/bs] int32 for rows m0 <= m < m1:
  *   Q4_0:   sum_{k in b} (q - 8) * xq[m][k]
  *   affine: sum_{k in g} q * xq[m][k]
@@ -182,6 +190,19 @@ int q4_gemm(int M, int K, int N, int bs, int fmt, int bits,
 int q4_debug_partials(int path, int M, int K, int N, int bs, int fmt, int bits,
                       const uint8_t* wq, const int8_t* xq, const int32_t* xsum,
                       int m0, int m1, int32_t* partials, void* stream);
+
+/*
+ * Debug view of the exact integer partials inside q4_gemv_fused: the fused
+ * decode kernel itself (every workgroup quantizes x into LDS and dots the
+ * weight codes against its own copy of the codes), compiled with the partials
+ * store in place of the float epilogue (tract PR #2432, "The kernel": the
+ * integer dot of every block is exact). x [1][K] float32 or bfloat16 (xdtype),
+ * 16-byte aligned; wq as q4_gemv; partials [N][K/bs] int32 as
+ * q4_debug_partials (Q4_0: sum (q - 8) * xq; affine: sum q * xq), where xq are
+ * the codes q4_quantize_act gives for x. K <= 32768.
+ */
+int q4_debug_partials_fused(int K, int N, int bs, int fmt, int bits, int xdtype, const void* x,
+                            const uint8_t* wq, int32_t* partials, void* stream);
 
 /*
  * Q4_K fused-dequant GEMV (M must be 1) and GEMM (any M >= 1) with float32

@@ -33,7 +33,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None

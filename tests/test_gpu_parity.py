@@ -941,3 +941,28 @@ def test_quantize_act_exact_reading(bs, nblocks, seed):
 
     assert check_exact_codes(standalone, bs, nblocks, seed) == []
     assert check_exact_codes(fused, bs, nblocks, seed) == []
+
+
+@pytest.mark.parametrize("fmt,bs,xdt,K,N", [("q4_0", 32, "f32", 4096, 4096), ("q4_0", 32, "bf16", 4096, 4096),
+                                            ("q4_0", 32, "f32", 8224, 37), ("affine", 64, "bf16", 4096, 1000),
+                                            ("affine", 128, "f32", 14336, 33), ("affine", 128, "bf16", 128, 17)])
+def test_gemv_fused_partials_bit_exact(fmt, bs, xdt, K, N):
+    # the production fused decode kernel (each workgroup quantizes x into its
+    # own LDS copy) with the partials store: every workgroup's integer path
+    print(f"case fused gemv partials {fmt} bs={bs} x={xdt} K={K} N={N}", flush=True)
+    if fmt == "q4_0" and K == 4096 and N == 4096:
+        wl, x, _, _, wts = workload_data("q4_0_decode_4096")
+        if xdt == "bf16":
+            x = synth.bf16_bits(x)
+    else:
+        rng = np.random.default_rng(K + N)
+        x32 = (rng.standard_normal((1, K)) * 2.0).astype(np.float32)
+        x32[0, rng.integers(0, K, max(1, K // 100))] *= 20.0
+        x = synth.bf16_bits(x32) if xdt == "bf16" else x32
+        w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+        wts = oracle.quantize_q4_0(w) if fmt == "q4_0" else oracle.quantize_affine(synth.bf16_bits(w), bs)
+    act = oracle.quantize_act(x, bs)
+    ref = oracle.q4_partials(wts[0], act[0], K, N, bs, FMT[fmt])[0]
+    got = q4.debug_partials_fused(fmt, bs, to_dev(x), to_dev(wts[0]))
+    _sync()
+    assert np.array_equal(to_np(got), ref)
