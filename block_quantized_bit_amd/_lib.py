@@ -24,7 +24,8 @@ Q4K_BLOCK_BYTES = 144
 EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_partials", "q4k_gemv", "q4k_gemm",
            "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string", "q4_packed_bytes", "q4_pack_weights",
            "q4_gemm_packed_work_bytes", "q4_gemm_packed", "q4_backward_work_bytes", "q4k_gemm_backward",
-           "q4_gemm_backward", "q4_measure_empty", "q4_measure_stream_read", "q4_debug_partials_fused")
+           "q4_gemm_backward", "q4_measure_empty", "q4_measure_stream_read", "q4_debug_partials_fused",
+           "q4k_gemm_backward_noalloc")
 _SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes", "q4_backward_work_bytes")
 
 
@@ -64,6 +65,7 @@ def lib() -> ctypes.CDLL:
         L.q4k_gemm_backward.argtypes = [I, I, I, P, P, P, P, P]
         L.q4_gemm_backward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
         L.q4_debug_partials_fused.argtypes = [I, I, I, I, I, I, P, P, P, P]
+        L.q4k_gemm_backward_noalloc.argtypes = [I, I, I, P, P, P, P]
         L.q4_measure_empty.argtypes = [I, I, P]
         L.q4_measure_stream_read.argtypes = [P, ctypes.c_size_t, I, I, ctypes.c_uint32, P, P]
         for name in EXPORTS:
@@ -267,6 +269,15 @@ def q4k_gemm_backward(blocks, dy, K: int, dx=None, work=None, stream=None):
     work = _backward_work(M, K, N, work, dy.device)
     _check(lib().q4k_gemm_backward(M, K, N, _ptr(blocks), _ptr(dy), _ptr(dx), _ptr(work), _stream(stream)),
            "q4k_gemm_backward")
+    return dx
+
+
+def q4k_gemm_backward_noalloc(blocks, dy, K: int, dx, stream=None):
+    """q4k_gemm_backward with the library's static per-device scratch buffer instead of a workspace (the
+    call allocates nothing; dx [M][K] float32 must be given). Calls that overlap on one GPU race."""
+    M, N = dy.shape
+    _check(lib().q4k_gemm_backward_noalloc(M, K, N, _ptr(blocks), _ptr(dy), _ptr(dx), _stream(stream)),
+           "q4k_gemm_backward_noalloc")
     return dx
 
 

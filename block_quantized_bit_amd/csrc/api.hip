@@ -71,6 +71,7 @@ const char* q4_status_string(int status) {
         case Q4_ERR_ALIGN: return "a pointer is not aligned as its argument requires";
         case Q4_ERR_HIP: return "a kernel launch failed";
         case Q4_ERR_RANGE: return "row range [m0, m1) is empty or outside [0, M]";
+        case Q4_ERR_SCRATCH: return "the call needs more scratch memory than the library's static per-device buffer (16 MiB); use the entry point that takes a workspace";
         default: return "unknown status";
     }
 }

@@ -83,7 +83,8 @@ typedef enum {
     Q4_ERR_FORMAT = 4,   /* unknown format or dtype, or a code width the entry point does not decode */
     Q4_ERR_ALIGN = 5,    /* a pointer is not aligned as its argument requires */
     Q4_ERR_HIP = 6,      /* a kernel launch failed */
-    Q4_ERR_RANGE = 7     /* row range [m0, m1) outside [0, M] or empty */
+    Q4_ERR_RANGE = 7,    /* row range [m0, m1) outside [0, M] or empty */
+    Q4_ERR_SCRATCH = 8   /* the call needs more scratch than the library's static per-device buffer (16 MiB) */
 } q4_status;
 
 enum { Q4_DT_F32 = 0, Q4_DT_BF16 = 1 };
@@ -302,6 +303,21 @@ int q4k_gemm_backward(int M, int K, int N, const void* blocks, const float* dy, 
 int q4_gemm_backward(int M, int K, int N, int bs, int fmt, int bits, const uint8_t* wq,
                      const void* wscale, const void* wbias, const float* dy, float* dx,
                      void* work, void* stream);
+
+/*
+ * q4k_gemm_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The partial sums live in a static
+ * device buffer of the library, one per GPU, of 16 MiB (16777216 bytes),
+ * held until the process ends; the call allocates nothing. A shape
+ * whose q4_backward_work_bytes(M, K, N) exceeds the capacity is rejected with
+ * Q4_ERR_SCRATCH before any launch (at K = 4096 and N = 14336 every M up to
+ * 256 fits). Calls on one GPU share its buffer: calls that overlap on one GPU
+ * (other streams or host threads) race and must be serialized by the caller.
+ * Other arguments, results and errors as q4k_gemm_backward.
+ */
+int q4k_gemm_backward_noalloc(int M, int K, int N, const void* blocks, const float* dy, float* dx,
+                              void* stream);
 
 /* Static name of a q4_status value ("unknown status" otherwise). */
 const char* q4_status_string(int status);

@@ -15,7 +15,7 @@ import pytest
 import block_quantized_bit_amd as q4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, DIM, BLOCK, FORMAT, ALIGN, HIP, RANGE = range(8)
+OK, NULL, DIM, BLOCK, FORMAT, ALIGN, HIP, RANGE, SCRATCH = range(9)
 # stand-ins for device pointers: never dereferenced, every call below fails validation first
 A = 0x100000
 MIS = 0x100001
@@ -33,7 +33,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None
@@ -219,3 +219,16 @@ def test_binding_raises_with_message():
         pytest.skip("host-only check")
     with pytest.raises(ValueError):
         q4.quantize_act(torch.zeros(2, 64), 32)   # host tensor: refused before any call
+
+
+def test_noalloc_backward_validation():
+    # shapes whose partial sums exceed the static 16 MiB buffer are refused before any launch
+    f = q4.lib().q4k_gemm_backward_noalloc
+    need = q4.lib().q4_backward_work_bytes(512, 14336, 4096)
+    assert need > 16 << 20
+    assert f(512, 14336, 4096, A, A, A, None) == SCRATCH
+    assert f(0, 256, 8, A, A, A, None) == DIM
+    assert f(4, 100, 8, A, A, A, None) == BLOCK
+    assert f(4, 256, 8, None, A, A, None) == NULL
+    assert f(4, 256, 8, MIS, A, A, None) == ALIGN
+    assert "16 MiB" in q4.status_string(SCRATCH)
