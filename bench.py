@@ -626,6 +626,17 @@ def main():
                               "GB/s": round(qbytes / t / 1e9, 1), "frac_hbm": round(qbytes / t / 1e9 / HBM_PEAK_GBS, 4),
                               "frac_fp32_peak_reference": round(flops / t / 1e12 / FP32_PEAK_TFLOPS, 4),
                               "matrix_unit": "f16 (float32-accurate split)"})
+            # the same product with the activations split once per call into a workspace (two launches)
+            work = torch.empty(int(q4.lib().q4k_gemm_work_bytes(16, g16.K)), dtype=torch.uint8, device=dev)
+            y16.fill_(float("nan"))
+            q4.q4k_gemm_work(blocks, x16, g16.N, y=y16, work=work)
+            torch.cuda.synchronize()
+            gw = gate(g16.name, y16)
+            entry["work_gate"] = gw
+            if gw["ok"]:
+                t = time_graphed(lambda: q4.q4k_gemm_work(blocks, x16, g16.N, y=y16, work=work), 200)
+                entry.update({"work_us": round(t * 1e6, 2), "work_GB/s": round(qbytes / t / 1e9, 1),
+                              "work_frac_hbm": round(qbytes / t / 1e9 / HBM_PEAK_GBS, 4)})
             secondary["q4k_gemm_16x4096x14336"] = entry
 
     if want("q4k_backward") or want("q4_backward"):

@@ -25,8 +25,8 @@ EXPORTS = ("q4_quantize_act", "q4_gemv", "q4_gemv_fused", "q4_gemm", "q4_debug_p
            "q4_quantize_weights", "q4k_quantize_weights", "q4_status_string", "q4_packed_bytes", "q4_pack_weights",
            "q4_gemm_packed_work_bytes", "q4_gemm_packed", "q4_backward_work_bytes", "q4k_gemm_backward",
            "q4_gemm_backward", "q4_measure_empty", "q4_measure_stream_read", "q4_debug_partials_fused",
-           "q4k_gemm_backward_noalloc")
-_SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes", "q4_backward_work_bytes")
+           "q4k_gemm_backward_noalloc", "q4k_gemm_work_bytes", "q4k_gemm_work")
+_SIZE_T_FUNCS = ("q4_packed_bytes", "q4_gemm_packed_work_bytes", "q4_backward_work_bytes", "q4k_gemm_work_bytes")
 
 
 class Q4Error(RuntimeError):
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.q4_gemm_backward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
         L.q4_debug_partials_fused.argtypes = [I, I, I, I, I, I, P, P, P, P]
         L.q4k_gemm_backward_noalloc.argtypes = [I, I, I, P, P, P, P]
+        L.q4k_gemm_work_bytes.argtypes = [I, I]
+        L.q4k_gemm_work.argtypes = [I, I, I, P, P, P, P, P]
         L.q4_measure_empty.argtypes = [I, I, P]
         L.q4_measure_stream_read.argtypes = [P, ctypes.c_size_t, I, I, ctypes.c_uint32, P, P]
         for name in EXPORTS:
@@ -277,7 +279,7 @@ def q4k_gemm_backward_noalloc(blocks, dy, K: int, dx, stream=None):
     call allocates nothing; dx [M][K] float32 must be given). Calls that overlap on one GPU race."""
     M, N = dy.shape
     _check(lib().q4k_gemm_backward_noalloc(M, K, N, _ptr(blocks), _ptr(dy), _ptr(dx), _stream(stream)),
-           "q4k_gemm_backward_noalloc")
+           "q4k_gemm_backward_noalloc", "q4k_gemm_work_bytes", "q4k_gemm_work")
     return dx
 
 
@@ -306,6 +308,23 @@ def q4k_gemm(blocks, x, N: int, y=None, stream=None):
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     _check(lib().q4k_gemm(M, K, N, _ptr(blocks), _ptr(x), _ptr(y), _stream(stream)), "q4k_gemm")
+    return y
+
+
+def q4k_gemm_work(blocks, x, N: int, y=None, work=None, stream=None):
+    """q4k_gemm with the activations split once per call into a workspace (two launches)."""
+    M, K = x.shape
+    nbytes = int(lib().q4k_gemm_work_bytes(M, K))
+    if nbytes == 0:
+        raise ValueError("invalid shape for the Q4_K GEMM (K must be a multiple of 256)")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if work is None:
+        work = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    elif work.numel() * work.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    _check(lib().q4k_gemm_work(M, K, N, _ptr(blocks), _ptr(x), _ptr(y), _ptr(work), _stream(stream)),
+           "q4k_gemm_work")
     return y
 
 

@@ -284,6 +284,20 @@ int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, 
     return hip_status(q4::launch_q4k_gemm(M, K, N, blocks, x, y, static_cast<hipStream_t>(stream)));
 }
 
+size_t q4k_gemm_work_bytes(int M, int K) {
+    if (M <= 0 || K <= 0 || K % 256 != 0 || M > (1 << 20)) return 0;
+    return q4::q4k_gemm_work_bytes(M, K);
+}
+
+int q4k_gemm_work(int M, int K, int N, const void* blocks, const float* x, float* y, void* work, void* stream) {
+    if (!blocks || !x || !y || !work) return Q4_ERR_NULL;
+    if (M <= 0 || N <= 0 || K <= 0 || M > (1 << 20)) return Q4_ERR_DIM;
+    if (K % 256 != 0) return Q4_ERR_BLOCK;
+    if (q4k_offsets_too_large(M, K, N) || q4::q4k_gemm_work_bytes(M, K) >= (1ull << 31)) return Q4_ERR_DIM;
+    if (!aligned(blocks, 16) || !aligned(x, 16) || !aligned(y, 4) || !aligned(work, 16)) return Q4_ERR_ALIGN;
+    return hip_status(q4::launch_q4k_gemm_work(M, K, N, blocks, x, y, work, static_cast<hipStream_t>(stream)));
+}
+
 int q4_quantize_weights(int N, int K, int bs, int fmt, int bits, int wdtype, const void* w, uint8_t* wq,
                         void* wscale, void* wbias, void* stream) {
     if (fmt != Q4_FMT_Q4_0 && fmt != Q4_FMT_AFFINE) return Q4_ERR_FORMAT;

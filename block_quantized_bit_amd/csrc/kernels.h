@@ -99,6 +99,12 @@ hipError_t launch_backward(int M, int K, int N, int fmt, int bs, const uint8_t* 
 
 hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
 hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream);
+// q4k_gemm with the activations split once per call into a workspace of
+// q4k_gemm_work_bytes(M, K) bytes (a split kernel, then the GEMM copying the
+// split tiles instead of forming them in every workgroup).
+size_t q4k_gemm_work_bytes(int M, int K);
+hipError_t launch_q4k_gemm_work(int M, int K, int N, const void* blocks, const float* x, float* y, void* work,
+                                hipStream_t stream);
 
 hipError_t launch_quantize_weights(int N, int K, int bs, int fmt, int bits, bool bf16, const void* w, uint8_t* wq,
                                    void* wscale, void* wbias, hipStream_t stream);

@@ -247,6 +247,18 @@ __device__ __forceinline__ float sum8(float v) {
     return v;
 }
 
+// Scale of a row's activations over a super-block, from the float4 each lane
+// holds (a wavefront holds the row): the largest magnitude mx = f * 2^E,
+// f in [0.5, 1) (E = -126 below the normal range), is brought into
+// [2^14, 2^15) by 2^(15 - E), at most 2^126 so that the scale and its inverse
+// stay normal floats. sc = 2^(15 - E), inv = 2^(E - 15).
+__device__ __forceinline__ void split_scale(const float4& v, float& sc, float& inv) {
+    const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    const int E = max((int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF) - 126, -111);
+    sc = __builtin_bit_cast(float, (uint32_t)(127 + 15 - E) << 23);
+    inv = __builtin_bit_cast(float, (uint32_t)(127 - 15 + E) << 23);
+}
+
 // Two codes (nibbles in bits 0..3 and 16..19 of t) as an exact f16 pair:
 // 0x6400 | q is the half 1024 + q, and subtracting 1024 leaves q.
 __device__ __forceinline__ uint32_t code_pair_f16(uint32_t t) {
@@ -305,12 +317,54 @@ struct Q4kStage {
     float inv[2][16];        // [buffer][row]: 2^-e
 };
 
-template <int W, int KP>
+// The activation tile of one 16-row group and super-block, split as the
+// kernel stages it, in 16-byte units: hi [16][256] f16 (units 0..511, row r
+// at 32 r), lo likewise (512..1023), the per-row sub-block sums [8][16] f32
+// (1024..1055) and the rows' 2^-e (1056..1059).
+constexpr int TILE_UNITS = 1060;
+
+// Splits x once per call into tiles (mt, sb) at ((mt * nsb + sb) * TILE_UNITS)
+// 16-byte units of `work`, with the same arithmetic as the in-kernel staging
+// of q4k_gemm_kernel. Grid (nsb, row tiles, 4): a workgroup of 4 wavefronts
+// takes 4 rows of a tile's super-block, one row per wavefront and one float4
+// per lane, so every row's scale is a wavefront reduction.
+__global__ __launch_bounds__(256) void q4k_split_kernel(int M, int K, const float* __restrict__ x,
+                                                        uint8_t* __restrict__ work) {
+    const int lane = threadIdx.x & 63, c4 = lane;
+    const int sb = blockIdx.x, mt = blockIdx.y, nsb = K >> 8;
+    const int r = 4 * (int)blockIdx.z + (int)(threadIdx.x >> 6);
+    const int m = mt * 16 + r;
+    const __amdgpu_buffer_rsrc_t r_x = rsrc(x, (uint32_t)((size_t)M * K * 4));
+    uint8_t* tile = work + ((size_t)mt * nsb + sb) * TILE_UNITS * 16;
+    _Float16* hi = reinterpret_cast<_Float16*>(tile);
+    _Float16* lo = hi + 16 * QK;
+    float* sum = reinterpret_cast<float*>(tile + 1024 * 16);
+    float* inv = sum + 8 * 16;
+    const uint32_t o = (m < M) ? (uint32_t)(((size_t)m * K + (size_t)sb * QK + 4 * c4) * 4) : OUT;
+    const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, o, 0, 0));
+    float sc, ivs;
+    split_scale(v, sc, ivs);
+    const float xs0 = v.x * sc, xs1 = v.y * sc, xs2 = v.z * sc, xs3 = v.w * sc;
+    const _Float16 h0 = (_Float16)xs0, h1 = (_Float16)xs1, h2 = (_Float16)xs2, h3 = (_Float16)xs3;
+    typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<v4h*>(hi + r * QK + 4 * c4) = v4h{h0, h1, h2, h3};
+    *reinterpret_cast<v4h*>(lo + r * QK + 4 * c4) =
+        v4h{(_Float16)(xs0 - (float)h0), (_Float16)(xs1 - (float)h1), (_Float16)(xs2 - (float)h2),
+            (_Float16)(xs3 - (float)h3)};
+    const float ssum = sum8((xs0 + xs1) + (xs2 + xs3));
+    if ((c4 & 7) == 0) sum[(c4 >> 3) * 16 + r] = ssum;
+    if (c4 == 0) inv[r] = ivs;
+}
+
+template <int W, int KP, bool PRESPLIT>
 __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ blocks,
-                                                               const float* __restrict__ x, float* __restrict__ y) {
+                                                               const float* __restrict__ x, float* __restrict__ y,
+                                                               const uint8_t* __restrict__ work) {
     constexpr int NTH = 64 * W;             // threads of one K range
     constexpr int XCH = 16 * QK / 4 / NTH;  // float4 of the activation tile per thread (16 / W)
     static_assert(XCH * NTH == 16 * QK / 4, "staging covers the tile");
+    constexpr int UPT = 1024 / NTH;         // PRESPLIT: hi / lo units of the split tile per thread
+    static_assert(UPT * NTH == 1024 && NTH >= 36, "the split tile is copied as UPT + 1 units per thread");
     __shared__ Q4kStage<W, KP> st[KP];
     // the wavefront index is uniform: the K range, and with it every load's scalar offset, stays in SGPRs
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -333,14 +387,28 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
     const uint32_t ow = (n < N) ? (uint32_t)((size_t)n * nsb * BLOCK_BYTES) : OUT;
 
     float4 rx[XCH];
+    uint4 ru[UPT], ru5;  // PRESPLIT: the tile's 16-byte units tp + NTH i, and unit 1024 + tp (tp < 36)
+    const __amdgpu_buffer_rsrc_t r_t =
+        rsrc(work, PRESPLIT ? (uint32_t)((size_t)((M + 15) / 16) * nsb * TILE_UNITS * 16) : 0u);
+    const uint32_t otile = (uint32_t)((size_t)blockIdx.y * nsb * TILE_UNITS * 16);
     uint4 rh;
     uint2 rq[4];
     auto load = [&](int sb) {  // super-blocks past the range read zero
         const bool in = sb < sb1;
+        if (PRESPLIT) {
+            const uint32_t so = in ? otile + (uint32_t)sb * TILE_UNITS * 16 : 0u;
 #pragma unroll
-        for (int i = 0; i < XCH; ++i)
-            rx[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? ox[i] : OUT,
-                                                                                     in ? sb * QK * 4 : 0, 0));
+            for (int i = 0; i < UPT; ++i)
+                ru[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      r_t, in ? (uint32_t)(tp + NTH * i) * 16 : OUT, so, 0));
+            ru5 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                r_t, (in && tp < 36) ? (uint32_t)(1024 + tp) * 16 : OUT, so, 0));
+        } else {
+#pragma unroll
+            for (int i = 0; i < XCH; ++i)
+                rx[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? ox[i] : OUT,
+                                                                                         in ? sb * QK * 4 : 0, 0));
+        }
         const uint32_t o = in ? ow : OUT, so = in ? (uint32_t)(sb * BLOCK_BYTES) : 0u;
         rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, so, 0));
 #pragma unroll
@@ -353,15 +421,25 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
     // and its sub-block sums are wavefront and 8-lane reductions.
     auto stage = [&](int b) {
         Q4kStage<W, KP>& S = st[p];
+        if (PRESPLIT) {  // a copy of the split tile into the padded LDS rows
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                const int u = tp + NTH * i, half = u >> 9, r = (u >> 5) & 15, c8 = u & 31;
+                v8h* dst = half ? S.lo[b] : S.hi[b];
+                dst[r * (XR / 8) + c8] = __builtin_bit_cast(v8h, ru[i]);
+            }
+            if (tp < 32)
+                *reinterpret_cast<uint4*>(&S.sum[b][0][0] + 4 * tp) = ru5;
+            else if (tp < 36)
+                *reinterpret_cast<uint4*>(&S.inv[b][4 * (tp - 32)]) = ru5;
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int idx = tp + NTH * i, r = idx >> 6, c4 = idx & 63;
             const float4 v = rx[i];
-            const float mx = wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-            // mx = f * 2^E, f in [0.5, 1) (E = -126 below the normal range); scale by 2^(15 - E),
-            // at most 2^126 so that the scale and its inverse stay normal floats
-            const int E = max((int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF) - 126, -111);
-            const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 15 - E) << 23);
+            float sc, ivs;
+            split_scale(v, sc, ivs);
             const float xs0 = v.x * sc, xs1 = v.y * sc, xs2 = v.z * sc, xs3 = v.w * sc;
             const _Float16 h0 = (_Float16)xs0, h1 = (_Float16)xs1, h2 = (_Float16)xs2, h3 = (_Float16)xs3;
             const _Float16 l0 = (_Float16)(xs0 - (float)h0), l1 = (_Float16)(xs1 - (float)h1);
@@ -371,7 +449,7 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
             *reinterpret_cast<v4h*>(reinterpret_cast<_Float16*>(S.lo[b]) + r * XR + 4 * c4) = v4h{l0, l1, l2, l3};
             const float ssum = sum8((xs0 + xs1) + (xs2 + xs3));
             if ((c4 & 7) == 0) S.sum[b][c4 >> 3][r] = ssum;
-            if (c4 == 0) S.inv[b][r] = __builtin_bit_cast(float, (uint32_t)(127 - 15 + E) << 23);
+            if (c4 == 0) S.inv[b][r] = ivs;
         }
     };
 
@@ -486,9 +564,30 @@ hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float*
     constexpr int W = 4;   // wavefronts (16 weight rows each) per K range
     constexpr int KP = 2;  // K ranges per workgroup (1: 34.3 us, 2: 29.5, 4: 30.0 at 16 x 4096 x 14336)
     const dim3 grid((unsigned)((N + 16 * W - 1) / (16 * W)), (unsigned)((M + 15) / 16));
-    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
-                       static_cast<const uint8_t*>(blocks), x, y);
+    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP, false>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
+                       static_cast<const uint8_t*>(blocks), x, y, nullptr);
     return hipGetLastError();
+}
+
+size_t q4k_gemm_work_bytes(int M, int K) { return (size_t)((M + 15) / 16) * (K / QK) * TILE_UNITS * 16; }
+
+template <int W, int KP>
+hipError_t launch_presplit(int M, int K, int N, const void* blocks, const float* x, float* y, const uint8_t* wk,
+                           hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 16 * W - 1) / (16 * W)), (unsigned)((M + 15) / 16));
+    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP, true>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
+                       static_cast<const uint8_t*>(blocks), x, y, wk);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_gemm_work(int M, int K, int N, const void* blocks, const float* x, float* y, void* work,
+                                hipStream_t stream) {
+    uint8_t* wk = static_cast<uint8_t*>(work);
+    hipLaunchKernelGGL(q4k_split_kernel, dim3((unsigned)(K / QK), (unsigned)((M + 15) / 16), 4), dim3(256), 0, stream,
+                       M, K, x, wk);
+    // the same launch shape as q4k_gemm (so the outputs are bit-identical); measured at 16 x 4096 x 14336:
+    // 4 x 2 wavefronts 20.8 us with the split, 4 x 4 20.8, 2 x 4 26.6, 2 x 2 23.5, 1 x 4 40.5
+    return launch_presplit<4, 2>(M, K, N, blocks, x, y, wk, stream);
 }
 
 }  // namespace q4

@@ -226,6 +226,20 @@ int q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y,
              void* stream);
 
 /*
+ * q4k_gemm with a caller workspace: the activations are split into the f16
+ * halves the matrix cores take (with the per-row, per-super-block power of
+ * two, the sub-block sums and the inverse scales) once per call by a first
+ * launch, and the GEMM copies the split tiles instead of forming them in
+ * every workgroup. Same arithmetic and results as q4k_gemm (bit-identical).
+ * work: caller-owned, 16-byte aligned, q4k_gemm_work_bytes(M, K) bytes
+ * (17 KB per 16 activation rows and 256 columns of K; 0 for invalid shapes);
+ * it holds the split tiles when the stream completes. Two launches on stream.
+ */
+size_t q4k_gemm_work_bytes(int M, int K);
+int q4k_gemm_work(int M, int K, int N, const void* blocks, const float* x, float* y,
+                  void* work, void* stream);
+
+/*
  * Weight quantization on the GPU (model preparation, not the hot path).
  * q4_quantize_weights: w [N][K] float32 or bfloat16 (wdtype) ->
  *   Q4_0 (bs 32):  i = first index of the largest |w| in the block,

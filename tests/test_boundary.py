@@ -33,7 +33,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     L = q4.lib()
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 23
     assert sorted(q4.EXPORTS) == names
     for name in names:
         assert getattr(L, name) is not None
@@ -232,3 +232,14 @@ def test_noalloc_backward_validation():
     assert f(4, 256, 8, None, A, A, None) == NULL
     assert f(4, 256, 8, MIS, A, A, None) == ALIGN
     assert "16 MiB" in q4.status_string(SCRATCH)
+
+
+def test_q4k_gemm_work_validation():
+    f = q4.lib().q4k_gemm_work
+    assert q4.lib().q4k_gemm_work_bytes(16, 4096) == 16 * 1060 * 16
+    assert q4.lib().q4k_gemm_work_bytes(17, 512) == 2 * 2 * 1060 * 16
+    assert q4.lib().q4k_gemm_work_bytes(4, 100) == 0 and q4.lib().q4k_gemm_work_bytes(0, 256) == 0
+    assert f(16, 256, 8, A, A, A, None, None) == NULL
+    assert f(0, 256, 8, A, A, A, A, None) == DIM
+    assert f(16, 300, 8, A, A, A, A, None) == BLOCK
+    assert f(16, 256, 8, A, A, A, MIS, None) == ALIGN

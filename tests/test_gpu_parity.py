@@ -966,3 +966,30 @@ def test_gemv_fused_partials_bit_exact(fmt, bs, xdt, K, N):
     got = q4.debug_partials_fused(fmt, bs, to_dev(x), to_dev(wts[0]))
     _sync()
     assert np.array_equal(to_np(got), ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(16, 4096, 14336), (1, 256, 7), (17, 512, 301), (33, 1280, 64)])
+def test_q4k_gemm_work_matches_q4k_gemm(M, K, N):
+    # the presplit path does the same arithmetic as q4k_gemm: bit-identical outputs, and within the
+    # tolerance of the oracle (sampled at the full 16 x 4096 x 14336 workload)
+    print(f"case q4k_gemm_work M={M} K={K} N={N}", flush=True)
+    if (M, K, N) == (16, 4096, 14336):
+        wl, x, _, _, blocks = workload_data("q4_k_gemm_16x4096x14336")
+    else:
+        rng = np.random.default_rng(M + K + N)
+        x = rng.standard_normal((M, K)).astype(np.float32)
+        x[M // 2] *= np.float32(1e-20)
+        blocks = oracle.quantize_q4k((0.02 * rng.standard_normal((N, K))).astype(np.float32))
+    gb, gx = to_dev(blocks), to_dev(x)
+    y0 = q4.q4k_gemm(gb, gx, N)
+    y1 = q4.q4k_gemm_work(gb, gx, N)
+    _sync()
+    a, b = to_np(y0), to_np(y1)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    if M * N <= 20000:
+        ref = oracle.q4k_gemm(blocks, x, K, N)
+        assert rel_rms(b, ref) <= TOL
+    else:
+        ms, ns = sample_pairs(M, N, 400, 5)
+        ref = oracle.q4k_gemm_sample(blocks, x, K, N, ms, ns)
+        assert rel_rms(b[ms, ns], ref) <= TOL
