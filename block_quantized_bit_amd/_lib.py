@@ -279,7 +279,7 @@ def q4k_gemm_backward_noalloc(blocks, dy, K: int, dx, stream=None):
     call allocates nothing; dx [M][K] float32 must be given). Calls that overlap on one GPU race."""
     M, N = dy.shape
     _check(lib().q4k_gemm_backward_noalloc(M, K, N, _ptr(blocks), _ptr(dy), _ptr(dx), _stream(stream)),
-           "q4k_gemm_backward_noalloc", "q4k_gemm_work_bytes", "q4k_gemm_work")
+           "q4k_gemm_backward_noalloc")
     return dx
 
 

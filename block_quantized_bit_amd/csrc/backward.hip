@@ -388,6 +388,258 @@ __global__ __launch_bounds__(64 * RW) void backward_rows_kernel(int M, int K, in
     }
 }
 
+// Q4_K input gradient on the f16 matrix cores (more than BWD_ROWS_MAX_M dY
+// rows). The same decomposition as backward_partial_kernel (a workgroup owns
+// one 256-wide column of K = one super-block, one 16-row tile of dY and one
+// range of weight rows, staged 64 rows at a time), with the product
+//   dx[m][k] = sum_n dy[m][n] (d[n] sc[n][s] q[n][k] - dmin[n] m[n][s])
+// taken as two f16 matrix products into one accumulator, with v_mfma_f32_16x16x32_f16:
+//   A = dy[m][n] d[n] * 2^e,    B = sc[n][s] q[n][k]      (exact in f16: <= 63 * 15)
+//   A = dy[m][n] dmin[n] * 2^e, B = -m[n][s]              (exact in f16: <= 63)
+// Each A enters as hi = f16(a) and lo = f16(a - hi); 2^e is a power of two per
+// dY row and stage that brings the row's largest |A| into [2^14, 2^15), so
+// hi + lo keep 22 of a's 24 significant bits, every product of a half with a
+// B value is exact in f32 and the stage's sum differs from the float32 one by
+// rounding only; it is scaled back by 2^-e into float accumulators. The B
+// operand holds, per lane, the codes of 8 consecutive weight rows for one
+// column k: the staging writes the column's code bytes transposed, [byte][row],
+// by 4 x 4 byte transposes (v_perm) of 4 rows x 8 bytes per thread.
+constexpr int CT = 72;  // bytes per transposed code row: 64 weight rows + 8 padding
+constexpr int AT = 72;  // halves per staged A row: 64 weight rows + 8 padding
+typedef _Float16 bv8h __attribute__((ext_vector_type(8)));
+typedef _Float16 bv4h __attribute__((ext_vector_type(4)));
+typedef _Float16 bv2h __attribute__((ext_vector_type(2)));
+
+struct BwdF16Lds {
+    uint8_t codes[128][CT];           // [qs byte j of the column][weight row n]
+    _Float16 ahi[16][AT], alo[16][AT];  // dy * d * 2^e as two halves, [m][n]
+    _Float16 bhi[16][AT], blo[16][AT];  // dy * dmin * 2^e
+    _Float16 sc[8][64], nsc[8][64];     // sc[s][n] and -1024 sc[s][n]
+    _Float16 nm[8][64];                 // -m[s][n]
+    float inv[16];                      // 2^-e per dY row
+};
+
+// Largest magnitude over the 16 lanes of a DPP row (values are magnitudes:
+// their bit patterns order as unsigned integers).
+__device__ __forceinline__ float row16_max(float f) {
+    uint32_t v = __builtin_bit_cast(uint32_t, f);
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, v);
+}
+
+// Two codes (bytes 0 and 1 of w, or 2 and 3 when HI) times their rows' sc:
+// 0x6400 | q is the half 1024 + q, and fma(1024 + q, sc, -1024 sc) = q sc exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t scaled_codes(uint32_t w, uint32_t scp, uint32_t nscp) {
+    const uint32_t h = __builtin_amdgcn_perm(0x64646464u, w, HI ? 0x04030402u : 0x04010400u);
+    const bv2h r = __builtin_elementwise_fma(__builtin_bit_cast(bv2h, h), __builtin_bit_cast(bv2h, scp),
+                                             __builtin_bit_cast(bv2h, nscp));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__global__ __launch_bounds__(BT, 2) void backward_q4k_f16_kernel(int M, int K, int N, int rows_per, int nr,
+                                                                 const uint8_t* __restrict__ w,
+                                                                 const float* __restrict__ dy,
+                                                                 float* __restrict__ work) {
+    __shared__ BwdF16Lds S[2];  // stage i in S[i & 1]; the next stage's loads wait in registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Workgroups are dispatched round-robin over the 8 XCDs. The 16 columns of
+    // one (row range, dY tile) read neighbouring 144-byte super-blocks of the
+    // same rows, whose cache lines they share, so they are mapped to one XCD
+    // (one L2): workgroup b runs on XCD b % 8, and the XCD's workgroups take
+    // the columns of its row groups x, x + 8, ... in turn.
+    const int nkb = K / KCOL, ngrp = nr * (int)((M + 15) / 16);
+    const int b = blockIdx.x, xcd = b & 7, t8 = b >> 3;
+    const int grp = (t8 / nkb) * 8 + xcd, kb = t8 % nkb;
+    if (grp >= ngrp) return;  // padding of the grid to whole rounds of 8
+    const int nc = grp % nr, m0 = (grp / nr) * 16;
+    const int nbeg = nc * rows_per, nend = min(N, nbeg + rows_per);
+    const int nst = nend > nbeg ? (nend - nbeg + RC - 1) / RC : 0;  // 64-row stages of the range
+    const int nsb = K / 256;
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(w, (uint32_t)((size_t)N * nsb * Q4K_BYTES));
+    const __amdgpu_buffer_rsrc_t r_dy = rsrc(dy, (uint32_t)((size_t)M * N * 4));
+
+    // staging roles of a thread within a 64-row stage
+    const int crg = tid >> 4, cbg = tid & 15;      // codes: rows 4 crg .. + 3, qs bytes 8 cbg .. + 7
+    const int hn = lane, hp = wave;                // header of row hn: 6-bit fields 4 hp .. 4 hp + 3
+    const int am = tid >> 4, an = 4 * (tid & 15);  // A operands: dY row am, weight rows an .. an + 3
+
+    // the next stage's loads wait in registers while a stage is computed
+    uint2 rc[4];
+    uint4 rh;
+    float rdy[4];
+    uint32_t rdd[4];
+    // Offsets are selected against the out-of-range offset with a bit operation
+    // (the buffer range check reads zero at offsets of 2^31 and above): with a
+    // condition the compiler branches around the load and, at the join, waits
+    // for every load in flight, which serialises the prefetch.
+    auto sel = [](uint32_t o, bool in) { return o | ((uint32_t)!in << 31); };
+    const uint32_t rowb = (uint32_t)nsb * Q4K_BYTES, colb = (uint32_t)kb * Q4K_BYTES;
+    const bool dyok = m0 + am < M;
+    const uint32_t dyrow = (uint32_t)(m0 + am) * (uint32_t)N * 4u;
+    auto load = [&](int r0) {  // rows past the range read zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = r0 + 4 * crg + i;
+            rc[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  r_w, sel((uint32_t)n * rowb + colb + 16u + 8u * (uint32_t)cbg, n < nend),
+                                                  0, 0));
+        }
+        {
+            const int n = r0 + hn;
+            rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               r_w, sel((uint32_t)n * rowb + colb, n < nend), 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = r0 + an + i;
+            const bool in = n < nend;
+            rdy[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   r_dy, sel(dyrow + 4u * (uint32_t)n, in && dyok), 0, 0));
+            rdd[i] = __builtin_amdgcn_raw_buffer_load_b32(r_w, sel((uint32_t)n * rowb + colb, in), 0, 0);
+        }
+    };
+    auto store = [&](BwdF16Lds& T) {
+        // codes: byte b of rows 4 crg .. + 3 into one dword of T.codes[8 cbg + b]
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+            const uint32_t w0 = hw ? rc[0].y : rc[0].x, w1 = hw ? rc[1].y : rc[1].x;
+            const uint32_t w2 = hw ? rc[2].y : rc[2].x, w3 = hw ? rc[3].y : rc[3].x;
+            const uint32_t t01a = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // r1.b1 r0.b1 r1.b0 r0.b0
+            const uint32_t t01b = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // r1.b3 r0.b3 r1.b2 r0.b2
+            const uint32_t t23a = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+            const uint32_t t23b = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+            const int j0 = 8 * cbg + 4 * hw;
+            *reinterpret_cast<uint32_t*>(&T.codes[j0][4 * crg]) = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(&T.codes[j0 + 1][4 * crg]) = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
+            *reinterpret_cast<uint32_t*>(&T.codes[j0 + 2][4 * crg]) = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(&T.codes[j0 + 3][4 * crg]) = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
+        }
+        // the sixteen 6-bit fields of the 96-bit little-endian string in h.y, h.z, h.w:
+        // field f < 8 is sc[f], f >= 8 is m[f - 8]
+        {
+            const uint64_t lo = (uint64_t)rh.y | ((uint64_t)rh.z << 32);  // bits 0..63
+            const uint64_t hi = (uint64_t)rh.z | ((uint64_t)rh.w << 32);  // bits 32..95
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = 4 * hp + i;
+                const uint32_t v = f < 8 ? (uint32_t)(lo >> (6 * f)) & 63u : (uint32_t)(hi >> (6 * f - 32)) & 63u;
+                const float fv = (float)v;
+                if (f < 8) {
+                    T.sc[f][hn] = (_Float16)fv;
+                    T.nsc[f][hn] = (_Float16)(-1024.0f * fv);
+                } else {
+                    T.nm[f - 8][hn] = (_Float16)(-fv);
+                }
+            }
+        }
+        // A operands of dY row am and weight rows an .. an + 3
+        {
+            float va[4], vb[4], mx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                va[i] = rdy[i] * half_to_float(rdd[i] & 0xFFFFu);
+                vb[i] = rdy[i] * half_to_float(rdd[i] >> 16);
+                mx = fmaxf(mx, fmaxf(fabsf(va[i]), fabsf(vb[i])));
+            }
+            mx = row16_max(mx);  // the 16 threads of dY row am form one DPP row
+            const int E = max((int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF) - 126, -111);
+            const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 15 - E) << 23);
+            if ((tid & 15) == 0) T.inv[am] = __builtin_bit_cast(float, (uint32_t)(127 - 15 + E) << 23);
+            bv4h ah, al, bh, bl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float xa = va[i] * sc, xb = vb[i] * sc;
+                ah[i] = (_Float16)xa;
+                al[i] = (_Float16)(xa - (float)ah[i]);
+                bh[i] = (_Float16)xb;
+                bl[i] = (_Float16)(xb - (float)bh[i]);
+            }
+            *reinterpret_cast<bv4h*>(&T.ahi[am][an]) = ah;
+            *reinterpret_cast<bv4h*>(&T.alo[am][an]) = al;
+            *reinterpret_cast<bv4h*>(&T.bhi[am][an]) = bh;
+            *reinterpret_cast<bv4h*>(&T.blo[am][an]) = bl;
+        }
+    };
+
+    // wavefront w owns chunk c = w of the column: qs bytes 32c .. 32c + 31, i.e.
+    // k = 64c + 32h + 16tt + col for the low (h = 0, sub-block 2c) and high
+    // (h = 1, sub-block 2c + 1) nibbles; tile t = 2h + tt
+    const int c = wave, g = lane >> 4, col = lane & 15;
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (nst > 0) {
+        load(nbeg);
+        store(S[0]);
+        load(nbeg + RC);
+    }
+    auto do_stage = [&](int i, auto par) {
+        constexpr int P = decltype(par)::value;  // i & 1
+        __syncthreads();  // stage i is in S[P]; every wavefront is done with S[P ^ 1]
+        if (i + 1 < nst) store(S[P ^ 1]);
+        load(nbeg + (i + 2) * RC);
+        const BwdF16Lds& T = S[P];
+        v4f D[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) D[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+            const int nb = 32 * step + 8 * g;  // this lane's 8 weight rows of the 32-row step
+            const bv8h Ahi = *reinterpret_cast<const bv8h*>(&T.ahi[col][nb]);
+            const bv8h Alo = *reinterpret_cast<const bv8h*>(&T.alo[col][nb]);
+            const bv8h Bhi = *reinterpret_cast<const bv8h*>(&T.bhi[col][nb]);
+            const bv8h Blo = *reinterpret_cast<const bv8h*>(&T.blo[col][nb]);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const uint2 cb = *reinterpret_cast<const uint2*>(&T.codes[32 * c + 16 * tt + col][nb]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int sbk = 2 * c + h;
+                    const uint32_t w0 = h ? (cb.x >> 4) & 0x0F0F0F0Fu : cb.x & 0x0F0F0F0Fu;
+                    const uint32_t w1 = h ? (cb.y >> 4) & 0x0F0F0F0Fu : cb.y & 0x0F0F0F0Fu;
+                    const uint4 scp = *reinterpret_cast<const uint4*>(&T.sc[sbk][nb]);
+                    const uint4 nsp = *reinterpret_cast<const uint4*>(&T.nsc[sbk][nb]);
+                    const uint4 q = make_uint4(scaled_codes<false>(w0, scp.x, nsp.x), scaled_codes<true>(w0, scp.y, nsp.y),
+                                               scaled_codes<false>(w1, scp.z, nsp.z), scaled_codes<true>(w1, scp.w, nsp.w));
+                    const bv8h Bq = __builtin_bit_cast(bv8h, q);
+                    const bv8h Bm = *reinterpret_cast<const bv8h*>(&T.nm[sbk][nb]);
+                    const int t = 2 * h + tt;
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bq, D[t], 0, 0, 0);
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bq, D[t], 0, 0, 0);
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Bhi, Bm, D[t], 0, 0, 0);
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Blo, Bm, D[t], 0, 0, 0);
+                }
+            }
+        }
+        // D layout: lane (col, g) holds rows 4g .. 4g + 3 of column col
+        const v4f iv = *reinterpret_cast<const v4f*>(&T.inv[4 * g]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(iv[r], D[t][r], acc[t][r]);
+    };
+    int i = 0;
+    for (; i + 1 < nst; i += 2) {
+        do_stage(i, std::integral_constant<int, 0>());
+        do_stage(i + 1, std::integral_constant<int, 1>());
+    }
+    if (i < nst) do_stage(i, std::integral_constant<int, 0>());
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int k = kb * KCOL + 64 * c + 32 * (t >> 1) + 16 * (t & 1) + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * g + r;
+            if (m < M) work[((size_t)nc * M + m) * K + k] = acc[t][r];
+        }
+    }
+}
+
 // dx[m][k] = sum over ranges c of work[c][m][k] in a fixed order: a workgroup
 // of 8 wavefronts takes 64 consecutive outputs; wavefront w sums ranges
 // w, w + 8, w + 16, ... in order (loads issued 16 at a time), and the eight
@@ -443,8 +695,14 @@ hipError_t launch_b(int M, int K, int N, const uint8_t* w, const void* ws, const
     const int nr = backward_ranges(M, K, N);
     const int rows_per = (N + nr - 1) / nr;
     const dim3 grid(K / KCOL, nr, (M + 15) / 16);
-    hipLaunchKernelGGL((backward_partial_kernel<FMTB, G>), grid, dim3(BT), 0, stream, M, K, N, rows_per, w,
-                       static_cast<const uint16_t*>(ws), static_cast<const uint16_t*>(wb), dy, work);
+    if (FMTB == 2) {
+        const long long ngrp = (long long)nr * ((M + 15) / 16);
+        const unsigned nwg = (unsigned)(((ngrp + 7) / 8) * 8 * (K / KCOL));
+        hipLaunchKernelGGL(backward_q4k_f16_kernel, dim3(nwg), dim3(BT), 0, stream, M, K, N, rows_per, nr, w, dy,
+                           work);
+    } else
+        hipLaunchKernelGGL((backward_partial_kernel<FMTB, G>), grid, dim3(BT), 0, stream, M, K, N, rows_per, w,
+                           static_cast<const uint16_t*>(ws), static_cast<const uint16_t*>(wb), dy, work);
     const long long total = (long long)M * K;
     hipLaunchKernelGGL(backward_reduce_kernel, dim3((unsigned)((total + 63) / 64)), dim3(64 * RED_W), 0, stream, total,
                        nr, work, dx);
