@@ -3,8 +3,30 @@
 // call returns its status without touching the device.
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <tuple>
+
 #include "q4.h"
 #include "kernels.h"
+
+namespace q4 {
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+    static std::mutex mu;
+    static std::set<std::tuple<int, const void*, size_t>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const auto key = std::make_tuple(dev, kernel, bytes);
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count(key)) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) done.insert(key);
+    return e;
+}
+
+}  // namespace q4
 
 namespace {
 

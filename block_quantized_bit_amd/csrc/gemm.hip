@@ -552,13 +552,8 @@ hipError_t launch_ksp(unsigned ntiles, int M, int K, int N, const uint8_t* wq, c
     const uint16_t* ws = static_cast<const uint16_t*>(wscale);
     const uint16_t* wb = static_cast<const uint16_t*>(wbias);
     auto k = partials ? gemm_kernel<FMT, G, true, PACKED, BITS, KSP> : gemm_kernel<FMT, G, false, PACKED, BITS, KSP>;
-    static bool attr[2] = {false, false};
-    if (!attr[partials != nullptr]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr[partials != nullptr] = true;
-    }
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(k), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(ntiles), dim3(NT * KSP), lds, stream, M, K, N, wq, ws, wb, xq, xs, xsum, y, partials);
     return hipGetLastError();
 }

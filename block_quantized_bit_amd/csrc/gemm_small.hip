@@ -341,12 +341,9 @@ hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale,
                      hipStream_t stream) {
     const size_t lds = sizeof(SmallLds<G, MT, BITS>);
     auto k = partials ? gemm_small_kernel<FMT, G, MT, true, BITS> : gemm_small_kernel<FMT, G, MT, false, BITS>;
-    static bool attr[2] = {false, false};
-    if (lds > 64 * 1024 && !attr[partials != nullptr]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (lds > 64 * 1024) {
+        const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(k), lds);
         if (e != hipSuccess) return e;
-        attr[partials != nullptr] = true;
     }
     hipLaunchKernelGGL(k, dim3((N + SN - 1) / SN), dim3(SNT), lds, stream, M, K, N, wq,
                        static_cast<const uint16_t*>(wscale), static_cast<const uint16_t*>(wbias), xq, xs, xsum, y,

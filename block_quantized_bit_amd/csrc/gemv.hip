@@ -745,13 +745,8 @@ hipError_t launch_rows_lds_fmt(int M, int K, int N, const uint8_t* wq, const voi
                               const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
                               hipStream_t stream) {
     auto k = gemv_rows_lds_kernel<FMT, G, GEMV_ROWS_LDS_MAX_M, PARTIALS>;
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, ROWS_LDS_MAX_BYTES);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(k), ROWS_LDS_MAX_BYTES);
+    if (e != hipSuccess) return e;
     const int grid = max(1, min(ROWS_LDS_GRID, (N + ROWS_LDS_WAVES - 1) / ROWS_LDS_WAVES));
     const int rpw = (N + ROWS_LDS_WAVES * grid - 1) / (ROWS_LDS_WAVES * grid);
     hipLaunchKernelGGL(k, dim3(grid), dim3(64 * ROWS_LDS_WAVES), gemv_rows_lds_bytes(M, K, G), stream, M, K, N, rpw,

@@ -7,6 +7,10 @@
 
 namespace q4 {
 
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (device, kernel, size); safe to call from several host threads.
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
 hipError_t launch_quantize_act(int M, int K, int bs, bool bf16, const void* x, int8_t* xq, float* xs,
                                int32_t* xsum, hipStream_t stream);
 // Same codes, with xs and xsum written group-major: [K/bs][M].

@@ -243,3 +243,17 @@ def test_q4k_gemm_work_validation():
     assert f(0, 256, 8, A, A, A, A, None) == DIM
     assert f(16, 300, 8, A, A, A, A, None) == BLOCK
     assert f(16, 256, 8, A, A, A, MIS, None) == ALIGN
+
+
+def test_offset_limits_of_the_w4a8_entry_points():
+    # Buffer loads address each operand with 32-bit byte offsets: weight codes of N * K * bits / 8 bytes and
+    # activation codes of M * K bytes must each stay below 2^31, else Q4_ERR_DIM before any launch.
+    L = q4.lib()
+    for entry in (L.q4_gemm, L.q4_gemv):
+        assert entry(*gemm_args(M=1, K=65536, N=65536)) == DIM                 # 2^31 bytes of 4-bit codes
+    assert L.q4_gemm(*gemm_args(M=1, K=65536, N=43691, fmt=1, bs=64, wb=A, bits=6)) == DIM
+    assert L.q4_gemm(*gemm_args(M=1, K=65536, N=32768, fmt=1, bs=64, wb=A, bits=8)) == DIM
+    assert L.q4_gemm(*gemm_args(M=32768, K=65536, N=8)) == DIM                # 2^31 bytes of activation codes
+    f = L.q4_debug_partials
+    assert f(1, 1, 65536, 65536, 32, 0, 4, A, A, A, 0, 1, A, None) == DIM
+    assert f(1, 32768, 65536, 8, 32, 0, 4, A, A, A, 0, 32768, A, None) == DIM
