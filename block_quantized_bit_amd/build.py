@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libq4.so")
 SOURCES = ["api.hip", "act_quant.hip", "gemv.hip", "gemm.hip", "gemm_small.hip", "backward.hip", "q4k.hip", "wquant.hip",
-           "measure.hip", "noalloc.hip"]
+           "measure.hip", "noalloc.hip", "rows_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,

@@ -8,10 +8,11 @@
 // MLX PR #4802: below M = 32 its int8 path is not taken and x is dequantized
 // instead; here the int8 path covers every M.
 //
-// Up to 4 rows with 4-bit codes go to the GEMV-shaped kernel in gemv.hip
+// One or two rows with 4-bit codes go to the GEMV-shaped kernel in gemv.hip
 // (activation codes of all rows in registers, 8 v_dot4 per row and block),
-// and 5 to 8 rows at N >= 4096 to its variant with the activations in LDS,
-// which are faster there; the kernel below covers the rest.
+// and 3 to 32 rows with 4-bit codes to the weight-streaming matrix-core kernel
+// in rows_mfma.hip, which are faster there; the kernel below covers 6- and
+// 8-bit codes and 33 to 64 rows.
 //
 // A workgroup owns 16 output columns and all M rows, so every weight block is
 // read once for all rows. K is walked in chunks (2048, 1024 or 512 wide, see
@@ -376,10 +377,10 @@ hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, con
                              const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                              int32_t* partials, hipStream_t stream) {
     if (M < 1 || M > GEMM_SMALL_MAX_M) return hipErrorInvalidValue;
-    if (gemv_rows_fits(M, K, bits))  // up to 4 rows of 4-bit codes: the GEMV-shaped kernel (gemv.hip)
+    if (gemv_rows_fits(M, K, bits))  // 1 or 2 rows of 4-bit codes: the GEMV-shaped kernel (gemv.hip)
         return launch_gemv_rows(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (gemv_rows_lds_preferred(M, K, N, fmt == 0 ? 32 : bs, bits))  // 5 to 8 rows, wide N: activations in LDS
-        return launch_gemv_rows_lds(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    if (rows_mfma_fits(M, K, fmt == 0 ? 32 : bs, fmt, bits))  // up to 32 rows of 4-bit codes (rows_mfma.hip)
+        return launch_rows_mfma(M, K, N, bs, fmt, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
     if (fmt == 0) {
         if (bits != 4) return hipErrorInvalidValue;
         return launch_fmt<0, 32>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);

@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(
     }
 }
 
-// Few-row variant (1 <= M <= 4 activation rows, 4-bit codes): the GEMV's
+// Few-row variant (1 or 2 activation rows, 4-bit codes): the GEMV's
 // weight stream and chunk mapping, with each pass's activation codes and
 // scales of all MR rows loaded into registers, so every unpacked weight chunk
 // feeds MR integer dots. A wavefront owns R consecutive weight rows.
@@ -452,187 +452,6 @@ __global__ __launch_bounds__(256) void gemv_rows_kernel(int M, int K, int N, con
     }
 }
 
-// Few-row variant for 5 to 8 activation rows (4-bit codes) with the
-// activation operands in LDS. Loading every row's codes into registers, as
-// gemv_rows_kernel does, makes each wavefront read all M x K codes through
-// its vector memory path; here a workgroup of 16 wavefronts copies the call's
-// activation codes, scales and code sums into LDS once -- codes as
-// [m][half][chunk] 16-byte units, so the lanes' reads of one half are
-// consecutive -- and each wavefront then streams its weight rows one pass
-// (4096 weights) at a time, the next pass's loads in flight, feeding every
-// unpacked chunk to M integer dots. The first activation and scale loads go
-// out before the first weight loads, so their LDS stores wait only for them.
-constexpr int ROWS_LDS_WAVES = 16;
-constexpr int ROWS_LDS_XP = 4;  // 16-byte activation units per thread loaded ahead of the weights
-constexpr int ROWS_LDS_SP = 2;  // activation scales (and code sums) per thread loaded ahead
-
-template <int FMT, int G, bool PARTIALS>
-struct RowPass {
-    uint4 w[U];
-    uint16_t s[U], b[U];
-
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r_w, __amdgpu_buffer_rsrc_t r_s,
-                                         __amdgpu_buffer_rsrc_t r_b, int row, int c0, int lane, int nchunks,
-                                         int ngroups, uint32_t rowbytes) {
-        constexpr int CPG = G / 32;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + lane + 64 * u;
-            const bool in = c < nchunks;
-            w[u] = __builtin_bit_cast(
-                uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, in ? row * rowbytes + 16u * c : OUT, 0, W_AUX));
-            if (!PARTIALS) {
-                const uint32_t so = in ? 2u * (row * ngroups + c / CPG) : OUT;
-                s[u] = __builtin_amdgcn_raw_buffer_load_b16(r_s, so, 0, 0);
-                if (FMT == 1) b[u] = __builtin_amdgcn_raw_buffer_load_b16(r_b, so, 0, 0);
-            }
-        }
-    }
-};
-
-// LDS index of 16-byte activation unit e (byte offset 16e of xq): row m,
-// chunk c, half h -> (2m + h) * nchunks + c.
-__device__ __forceinline__ int act_unit_slot(int e, int nchunks) {
-    const int m = e / (2 * nchunks), u = e - m * 2 * nchunks;
-    return (2 * m + (u & 1)) * nchunks + (u >> 1);
-}
-
-template <int FMT, int G, int MR, bool PARTIALS>
-__global__ __launch_bounds__(64 * ROWS_LDS_WAVES) void gemv_rows_lds_kernel(
-    int M, int K, int N, int rows_per_wave, const uint8_t* __restrict__ wq, const uint16_t* __restrict__ wscale,
-    const uint16_t* __restrict__ wbias, const int8_t* __restrict__ xq, const float* __restrict__ xs,
-    const int32_t* __restrict__ xsum, float* __restrict__ y, int32_t* __restrict__ partials) {
-    constexpr int CPG = G / 32;
-    constexpr int NT = 64 * ROWS_LDS_WAVES;
-    extern __shared__ __attribute__((aligned(16))) uint4 xl[];
-    const int tid = (int)threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row0 = (blockIdx.x * ROWS_LDS_WAVES + wave) * rows_per_wave;
-    const int nrows = max(0, min(rows_per_wave, N - row0));
-    const int nchunks = K >> 5, ngroups = K / G;
-    const uint32_t rowbytes = (uint32_t)(K >> 1);
-    const int units = M * 2 * nchunks;  // 16-byte units of activation codes
-    const int nsc = M * ngroups;
-    float* xsl = reinterpret_cast<float*>(xl + units);  // [M][ngroups]
-    int32_t* sxl = reinterpret_cast<int32_t*>(xsl + nsc);
-
-    const __amdgpu_buffer_rsrc_t r_w = rsrc(wq + (size_t)row0 * rowbytes, nrows * rowbytes);
-    const __amdgpu_buffer_rsrc_t r_s = rsrc(wscale + (size_t)row0 * ngroups, PARTIALS ? 0u : nrows * ngroups * 2u);
-    const __amdgpu_buffer_rsrc_t r_b =
-        rsrc(wbias + (size_t)row0 * ngroups, (PARTIALS || FMT == 0) ? 0u : nrows * ngroups * 2u);
-    const __amdgpu_buffer_rsrc_t r_a = rsrc(xq, (uint32_t)M * (uint32_t)K);
-    const __amdgpu_buffer_rsrc_t r_xs = rsrc(xs, PARTIALS ? 0u : (uint32_t)nsc * 4u);
-    const __amdgpu_buffer_rsrc_t r_sx = rsrc(xsum, (uint32_t)nsc * 4u);
-
-    // activation loads first (offsets past the operands read zero), then the
-    // first pass of weights
-    uint4 xv[ROWS_LDS_XP];
-    float av[ROWS_LDS_SP];
-    int32_t sv[ROWS_LDS_SP];
-#pragma unroll
-    for (int i = 0; i < ROWS_LDS_XP; ++i) {
-        const int e = tid + NT * i;
-        xv[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_a, e < units ? 16u * e : OUT, 0, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < ROWS_LDS_SP; ++i) {
-        const int e = tid + NT * i;
-        const uint32_t o = e < nsc ? 4u * e : OUT;
-        av[i] = PARTIALS ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, o, 0, 0));
-        sv[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_sx, o, 0, 0);
-    }
-    const int npass = (nchunks + 64 * U - 1) / (64 * U);
-    const int steps = nrows * npass;
-    RowPass<FMT, G, PARTIALS> cur;
-    cur.load(r_w, r_s, r_b, 0, 0, lane, nchunks, ngroups, rowbytes);
-#pragma unroll
-    for (int i = 0; i < ROWS_LDS_XP; ++i) {
-        const int e = tid + NT * i;
-        if (e < units) xl[act_unit_slot(e, nchunks)] = xv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < ROWS_LDS_SP; ++i) {
-        const int e = tid + NT * i;
-        if (e < nsc) {
-            xsl[e] = av[i];
-            sxl[e] = sv[i];
-        }
-    }
-    // the rest (long rows or many of them) after the weights
-    for (int e = tid + NT * ROWS_LDS_XP; e < units; e += NT)
-        xl[act_unit_slot(e, nchunks)] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_a, 16u * e, 0, 0));
-    for (int e = tid + NT * ROWS_LDS_SP; e < nsc; e += NT) {
-        xsl[e] = PARTIALS ? 0.0f : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_xs, 4u * e, 0, 0));
-        sxl[e] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_sx, 4u * e, 0, 0);
-    }
-    __syncthreads();
-
-    float acc[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
-    for (int t = 0; t < steps; ++t) {
-        const int row = t / npass, c0 = (t - row * npass) * 64 * U;
-        RowPass<FMT, G, PARTIALS> nxt;
-        if (t + 1 < steps) {
-            const int r1 = (t + 1) / npass;
-            nxt.load(r_w, r_s, r_b, r1, (t + 1 - r1 * npass) * 64 * U, lane, nchunks, ngroups, rowbytes);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + lane + 64 * u;
-            const int cc = min(c, nchunks - 1);  // chunks past K: zero codes and scales, LDS read kept in range
-            const int g = cc / CPG;
-            const uint4 w = cur.w[u];
-            const uint32_t lo[4] = {lo_nibbles(w.x), lo_nibbles(w.y), lo_nibbles(w.z), lo_nibbles(w.w)};
-            const uint32_t hi[4] = {hi_nibbles(w.x), hi_nibbles(w.y), hi_nibbles(w.z), hi_nibbles(w.w)};
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                if (m >= M) break;
-                const uint4 xa = xl[(2 * m) * nchunks + cc], xb = xl[(2 * m + 1) * nchunks + cc];
-                int dot = 0;
-                dot = __builtin_amdgcn_sdot4((int)lo[0], (int)xa.x, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)lo[1], (int)xa.y, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)lo[2], (int)xa.z, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)lo[3], (int)xa.w, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)hi[0], (int)xb.x, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)hi[1], (int)xb.y, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)hi[2], (int)xb.z, dot, false);
-                dot = __builtin_amdgcn_sdot4((int)hi[3], (int)xb.w, dot, false);
-                const int sx = sxl[m * ngroups + g];
-                if (PARTIALS) {
-                    int p = dot;
-                    if (FMT == 0) {
-                        p = dot - 8 * sx;
-                    } else {
-#pragma unroll
-                        for (int off = 1; off < CPG; off <<= 1) p += __shfl_xor(p, off, 64);
-                    }
-                    if (c < nchunks && (c % CPG) == 0) partials[((size_t)m * N + row0 + row) * ngroups + c / CPG] = p;
-                } else if (FMT == 0) {
-                    const int pq = dot - 8 * sx;  // sum (q - 8) * xq over the block
-                    acc[m] += (half_to_float(cur.s[u]) * xsl[m * ngroups + g]) * (float)pq;
-                } else {
-                    const float a = xsl[m * ngroups + g];
-                    acc[m] += a * (bf16_to_float(cur.s[u]) * (float)dot);
-                    const float bt = a * (bf16_to_float(cur.b[u]) * (float)sx);
-                    acc[m] += ((c % CPG) == 0) ? bt : 0.0f;
-                }
-            }
-        }
-        if (!PARTIALS && t - row * npass == npass - 1) {  // the row's last pass
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                if (m >= M) break;
-                const float v = wave_sum(acc[m]);
-                if (lane == 0) y[(size_t)m * N + row0 + row] = v;
-                acc[m] = 0.0f;
-            }
-        }
-        cur = nxt;
-    }
-}
-
 // Launch shapes. Plain GEMV (codes given): one row per wavefront, 8 wavefronts
 // per workgroup, codes read from global memory. Fused: one row per wavefront,
 // 16 wavefronts per workgroup sharing the quantization of x into LDS. The
@@ -735,25 +554,9 @@ hipError_t launch_rows_fmt(int M, int K, int N, const uint8_t* wq, const void* w
                            hipStream_t stream) {
     if (M == 1)
         return launch_rows_mr<FMT, G, 1, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    if (M == 2)
-        return launch_rows_mr<FMT, G, 2, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    return launch_rows_mr<FMT, G, 4, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
+    return launch_rows_mr<FMT, G, 2, PARTIALS>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
 }
 
-template <int FMT, int G, bool PARTIALS>
-hipError_t launch_rows_lds_fmt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
-                              const int8_t* xq, const float* xs, const int32_t* xsum, float* y, int32_t* partials,
-                              hipStream_t stream) {
-    auto k = gemv_rows_lds_kernel<FMT, G, GEMV_ROWS_LDS_MAX_M, PARTIALS>;
-    const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(k), ROWS_LDS_MAX_BYTES);
-    if (e != hipSuccess) return e;
-    const int grid = max(1, min(ROWS_LDS_GRID, (N + ROWS_LDS_WAVES - 1) / ROWS_LDS_WAVES));
-    const int rpw = (N + ROWS_LDS_WAVES * grid - 1) / (ROWS_LDS_WAVES * grid);
-    hipLaunchKernelGGL(k, dim3(grid), dim3(64 * ROWS_LDS_WAVES), gemv_rows_lds_bytes(M, K, G), stream, M, K, N, rpw,
-                       wq, static_cast<const uint16_t*>(wscale), static_cast<const uint16_t*>(wbias), xq, xs, xsum, y,
-                       partials);
-    return hipGetLastError();
-}
 
 template <int FMT, int G>
 hipError_t launch_rows_p(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias,
@@ -765,39 +568,6 @@ hipError_t launch_rows_p(int M, int K, int N, const uint8_t* wq, const void* wsc
 }
 
 }  // namespace
-
-size_t gemv_rows_lds_bytes(int M, int K, int bs) { return (size_t)M * K + 8 * (size_t)M * (K / bs); }
-
-bool gemv_rows_lds_fits(int M, int K, int bs, int bits) {
-    return bits == 4 && M >= 1 && M <= GEMV_ROWS_LDS_MAX_M && K >= 32 && K % bs == 0 &&
-           gemv_rows_lds_bytes(M, K, bs) <= (size_t)ROWS_LDS_MAX_BYTES;
-}
-
-bool gemv_rows_lds_preferred(int M, int K, int N, int bs, int bits) {
-    return M > GEMV_ROWS_MAX_M && N >= GEMV_ROWS_LDS_MIN_N && gemv_rows_lds_fits(M, K, bs, bits);
-}
-
-hipError_t launch_gemv_rows_lds(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
-                                const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
-                                int32_t* partials, hipStream_t stream) {
-    if (!gemv_rows_lds_fits(M, K, fmt == 0 ? 32 : bs, 4)) return hipErrorInvalidValue;
-    if (fmt == 0) {
-        if (partials)
-            return launch_rows_lds_fmt<0, 32, true>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-        return launch_rows_lds_fmt<0, 32, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    }
-    if (bs == 64) {
-        if (partials)
-            return launch_rows_lds_fmt<1, 64, true>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-        return launch_rows_lds_fmt<1, 64, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    }
-    if (bs == 128) {
-        if (partials)
-            return launch_rows_lds_fmt<1, 128, true>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-        return launch_rows_lds_fmt<1, 128, false>(M, K, N, wq, wscale, wbias, xq, xs, xsum, y, partials, stream);
-    }
-    return hipErrorInvalidValue;
-}
 
 bool gemv_rows_fits(int M, int K, int bits) { return bits == 4 && M >= 1 && M <= GEMV_ROWS_MAX_M && K >= 32; }
 

@@ -57,31 +57,26 @@ hipError_t launch_gemm_small(int M, int K, int N, int bs, int fmt, int bits, con
 
 // Few-row GEMV (1 <= M <= GEMV_ROWS_MAX_M, 4-bit codes): the decode GEMV's
 // weight stream with the activation codes of all rows in registers. Taken by
-// launch_gemm_small where gemv_rows_fits. Same arguments as launch_gemm.
-constexpr int GEMV_ROWS_MAX_M = 4;
+// launch_gemm_small where gemv_rows_fits (Q4_0 at M = 2, cold weights: 4.7 us
+// at 4096 x 4096, 9.7 us at N = 14336, 10.8 us at K = 14336, against 4.9,
+// 12.1 and 13.2 us for the matrix-core kernel below; from 3 rows on that one
+// is as fast or faster). Same arguments as launch_gemm.
+constexpr int GEMV_ROWS_MAX_M = 2;
 bool gemv_rows_fits(int M, int K, int bits);
 hipError_t launch_gemv_rows(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
                             const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
                             int32_t* partials, hipStream_t stream);
 
-// Few-row GEMV with the activation operands staged in LDS once per workgroup
-// (4-bit codes, M*K codes plus 8 bytes of scale and code sum per (row, block
-// or group) within ROWS_LDS_MAX_BYTES). launch_gemm_small takes it for
-// GEMV_ROWS_MAX_M < M <= GEMV_ROWS_LDS_MAX_M when N fills one workgroup of 16
-// weight rows per CU (measured at K = 4096, Q4_0, N = 4096: 6.4 us at M = 5
-// and 7.7 us at M = 8 against 8.2-8.3 us for the MFMA kernel; N = 14336, M = 8:
-// 20.2 against 27.3 us; at 12 and 16 rows, or N = 1000, the MFMA kernel is
-// faster). Same arguments as launch_gemm.
-constexpr int GEMV_ROWS_LDS_MAX_M = 8;
-constexpr int GEMV_ROWS_LDS_MIN_N = 4096;
-constexpr int ROWS_LDS_MAX_BYTES = 160 * 1024;
-constexpr int ROWS_LDS_GRID = 256;  // workgroups of 16 wavefronts: one per CU
-size_t gemv_rows_lds_bytes(int M, int K, int bs);
-bool gemv_rows_lds_fits(int M, int K, int bs, int bits);
-bool gemv_rows_lds_preferred(int M, int K, int N, int bs, int bits);
-hipError_t launch_gemv_rows_lds(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
-                                const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
-                                int32_t* partials, hipStream_t stream);
+// Few-row product on the int8 matrix cores with the decode GEMV's weight
+// stream (rows_mfma.hip): 4-bit Q4_0 or affine codes, M <= ROWS_MFMA_MAX_M,
+// a workgroup of 16 wavefronts per 16 weight rows. launch_gemm_small takes it
+// for GEMV_ROWS_MAX_M < M <= ROWS_MFMA_MAX_M. Same arguments as launch_gemm.
+constexpr int ROWS_MFMA_MAX_M = 32;
+bool rows_mfma_fits(int M, int K, int bs, int fmt, int bits);
+hipError_t launch_rows_mfma(int M, int K, int N, int bs, int fmt, const uint8_t* wq, const void* wscale,
+                            const void* wbias, const int8_t* xq, const float* xs, const int32_t* xsum, float* y,
+                            int32_t* partials, hipStream_t stream);
+
 
 // Packed weights for the tiled GEMM (layout in include/q4.h, q4_pack_weights).
 size_t packed_code_bytes(int K, int N);

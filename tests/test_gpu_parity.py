@@ -382,19 +382,21 @@ def test_small_gemm_dispatch_boundary():
         assert rel_rms(to_np(y), ref[:m]) <= TOL, m
 
 
-@pytest.mark.parametrize("M", [3, 6, 16, 100])
+@pytest.mark.parametrize("M", [2, 3, 16, 40, 100])
 def test_gemm_activation_row_extremes(M):
     # An all-zero activation row (scale 0, codes 0) must give exact zeros, and
     # rows scaled by 1e-30 and 1e30 must match the oracle, on every q4_gemm path
-    # at N = 4096: 3 rows take the register GEMV-shaped kernel, 6 its LDS
-    # variant, 16 the MFMA few-row kernel and 100 the tiled kernel.
+    # at N = 4096: 2 rows take the register GEMV-shaped kernel, 3 and 16 the
+    # weight-streaming matrix-core kernel, 40 the staged few-row MFMA kernel and
+    # 100 the tiled kernel.
     print(f"case gemm activation row extremes M={M}", flush=True)
     K, N = 512, 4096
     rng = np.random.default_rng(9000 + M)
     x = rng.standard_normal((M, K)).astype(np.float32)
     x[0] = 0.0
     x[1] *= np.float32(1e-30)
-    x[2] *= np.float32(1e30)
+    if M > 2:
+        x[2] *= np.float32(1e30)
     act = oracle.quantize_act(x, 32)
     wts = oracle.quantize_q4_0((0.02 * rng.standard_normal((N, K))).astype(np.float32))
     y = q4.gemm("q4_0", 32, *_wts_dev("q4_0", wts), *[to_dev(a) for a in act])
@@ -407,15 +409,16 @@ def test_gemm_activation_row_extremes(M):
         assert rel_rms(got[m], ref[m]) <= TOL, m
 
 
-def test_small_gemm_rows_lds_boundary():
-    # at N = 4096: 4 rows take the register GEMV-shaped kernel, 5 and 8 its LDS
-    # variant, 9 the MFMA kernel; K = 16416 at 8 rows needs more LDS than a
-    # workgroup has and goes to the MFMA kernel too. All against the oracle.
-    print("case small rows/lds/mfma boundary M=4,5,8,9", flush=True)
-    wts, act = _partials_case("affine", 128, 9, 1024, 4096, 4343)
+def test_small_gemm_kernel_boundaries():
+    # at N = 4096: 2 rows take the register GEMV-shaped kernel, 3 to 32 the
+    # weight-streaming matrix-core kernel (one 16-row tile up to 16 rows, two
+    # from 17), 33 the staged few-row MFMA kernel; K = 16416 at 8 rows gives
+    # each wavefront more than four quads (four in flight). All against the oracle.
+    print("case small kernel boundaries M=2,3,16,17,32,33", flush=True)
+    wts, act = _partials_case("affine", 128, 33, 1024, 4096, 4343)
     g = _wts_dev("affine", wts)
     ref = _oracle_y("affine", wts, act, 1024, 4096, 128)
-    for m in (4, 5, 8, 9):
+    for m in (2, 3, 16, 17, 32, 33):
         y = q4.gemm("affine", 128, *g, *[to_dev(a[:m]) for a in act])
         _sync()
         assert rel_rms(to_np(y), ref[:m]) <= TOL, m
@@ -427,7 +430,7 @@ def test_small_gemm_rows_lds_boundary():
 
 @pytest.mark.parametrize("fmt,bs,M,N", [("q4_0", 32, 32, 16), ("affine", 64, 17, 20)])
 def test_small_gemm_max_k(fmt, bs, M, N):
-    # K = 32768: 16 chunks of 2048 staged through LDS
+    # K = 32768: the longest rows, many quads per wavefront
     print(f"case small gemm max K {fmt} M={M} N={N}", flush=True)
     K = 32768
     wts, act = _partials_case(fmt, bs, M, K, N, 99 + M)
