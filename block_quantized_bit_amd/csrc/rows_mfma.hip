@@ -103,7 +103,11 @@ size_t rows_mfma_lds(int fmt, int mt) { return (size_t)RW * wave_lds_bytes(fmt, 
 // DEPTH: quads in flight per wavefront (2, or 4 for long rows). With one
 // 16-row tile and two quads in flight the kernel fits 64 registers, so two
 // workgroups share a CU.
-template <int FMT, int G, int MT, bool PARTIALS, int DEPTH>
+// HALF (at most 8 activation rows): one 128-bit load per quad brings rows
+// 0..7 of the activation tile, lanes c < 8 taking the first and lanes c + 8
+// the second half of row c's block; after the transpose a DPP row rotation by
+// 8 lanes hands each lane c < 8 its second-half dwords.
+template <int FMT, int G, int MT, bool PARTIALS, int DEPTH, bool HALF>
 __global__ __launch_bounds__(RNT, (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 64)) ? 8 : 4) void rows_mfma_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
                                                        const uint16_t* __restrict__ wscale,
                                                        const uint16_t* __restrict__ wbias,
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(RNT, (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 6
                                                        int32_t* __restrict__ partials) {
     constexpr bool AFF = FMT == 1;
     constexpr int MR = 16 * MT;
+    static_assert(!HALF || MT == 1, "the half tile is one 16-row tile");
     using Q = Quad<MT>;
     constexpr int SPG = G / 32;   // blocks per group
     constexpr int NS = 4 / SPG;   // groups per quad
@@ -158,6 +163,12 @@ __global__ __launch_bounds__(RNT, (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 6
         const bool in = blk < nb;
         t.w = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, sel(c * rowbytes + 16u * blk, in), 0, W_AUX));
+        if (HALF) {
+            const int m = c & 7;
+            const uint32_t o = sel((uint32_t)m * (uint32_t)K + 32u * blk + 16u * (c >> 3), in && m < M);
+            t.a[0][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_a, o, 0, 0));
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < MT; ++u) {
             const int m = 16 * u + c;
@@ -201,8 +212,15 @@ __global__ __launch_bounds__(RNT, (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 6
         uint32_t w[4] = {t.w.x, t.w.y, t.w.z, t.w.w};
         uint32_t a[MT][8];
         transpose4(w[0], w[1], w[2], w[3]);
+        if (HALF) {
+            a[0][0] = t.a[0][0].x, a[0][1] = t.a[0][0].y, a[0][2] = t.a[0][0].z, a[0][3] = t.a[0][0].w;
+            transpose4(a[0][0], a[0][1], a[0][2], a[0][3]);
 #pragma unroll
-        for (int u = 0; u < MT; ++u) {
+            for (int k = 0; k < 4; ++k)  // row_ror:8 within each 16-lane row
+                a[0][4 + k] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a[0][k], 0x128, 0xF, 0xF, false);
+        }
+#pragma unroll
+        for (int u = 0; u < MT && !HALF; ++u) {
             a[u][0] = t.a[u][0].x, a[u][1] = t.a[u][0].y, a[u][2] = t.a[u][0].z, a[u][3] = t.a[u][0].w;
             a[u][4] = t.a[u][1].x, a[u][5] = t.a[u][1].y, a[u][6] = t.a[u][1].z, a[u][7] = t.a[u][1].w;
             transpose4(a[u][0], a[u][1], a[u][2], a[u][3]);
@@ -320,11 +338,19 @@ template <int FMT, int G, int MT>
 hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale, const void* wbias, const int8_t* xq,
                      const float* xs, const int32_t* xsum, float* y, int32_t* partials, hipStream_t stream) {
     const size_t lds = rows_mfma_lds(FMT, MT);
-    // one 16-row tile: four quads in flight once a wavefront has at least four to do
+    // one 16-row tile: four quads in flight once a wavefront has at least four
+    // to do; up to 8 rows: the half tile
     constexpr int DEEP = MT == 1 ? 4 : 2;
     const bool deep = (K / 128) >= 4 * RW;
-    auto k = partials ? (deep ? rows_mfma_kernel<FMT, G, MT, true, DEEP> : rows_mfma_kernel<FMT, G, MT, true, 2>)
-                      : (deep ? rows_mfma_kernel<FMT, G, MT, false, DEEP> : rows_mfma_kernel<FMT, G, MT, false, 2>);
+    decltype(&rows_mfma_kernel<FMT, G, MT, true, 2, false>) k;
+    if (MT == 1 && M <= 8)
+        k = partials ? (deep ? rows_mfma_kernel<FMT, G, MT, true, DEEP, MT == 1>
+                             : rows_mfma_kernel<FMT, G, MT, true, 2, MT == 1>)
+                     : (deep ? rows_mfma_kernel<FMT, G, MT, false, DEEP, MT == 1>
+                             : rows_mfma_kernel<FMT, G, MT, false, 2, MT == 1>);
+    else
+        k = partials ? (deep ? rows_mfma_kernel<FMT, G, MT, true, DEEP, false> : rows_mfma_kernel<FMT, G, MT, true, 2, false>)
+                     : (deep ? rows_mfma_kernel<FMT, G, MT, false, DEEP, false> : rows_mfma_kernel<FMT, G, MT, false, 2, false>);
     if (lds > 64 * 1024) {
         const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(k), lds);
         if (e != hipSuccess) return e;
