@@ -640,6 +640,230 @@ __global__ __launch_bounds__(BT, 2) void backward_q4k_f16_kernel(int M, int K, i
     }
 }
 
+// Q4_0 input gradient on the f16 matrix cores (more than BWD_ROWS_MAX_M dY
+// rows), with the decomposition of backward_q4k_f16_kernel (one 256-wide
+// column of K = 8 blocks, one 16-row tile of dY, one range of weight rows,
+// staged 64 rows at a time). The block scale d varies along K within the
+// column, so it goes with the codes: per stage and block column b,
+//   B = d[n][b] * 2^-t_b * (q[n][k] - 8),   A = dy[m][n] * 2^e
+// where 2^-t_b brings the stage's largest |d| of column b into [2^10, 2^11)
+// (|B| < 2^14: no f16 overflow whatever d), and B enters as hi = f16(B) and
+// lo = f16(d' (q - 8) - hi), which is exact: d' (q - 8) has at most 15
+// significant bits. A is the dY tile as hi/lo halves with a power of two per
+// dY row and stage, as in the Q4_K kernel. Each (tile, 32-row step) is four
+// products (hi.hi, hi.lo, lo.hi, lo.lo) into one accumulator, scaled back by
+// 2^-e * 2^t_b (exact) into the float sums.
+struct BwdQ0Lds {
+    uint8_t codes[128][CT];             // [code byte j of the column][weight row n]
+    _Float16 ahi[16][AT], alo[16][AT];  // dy * 2^e as two halves, [m][n]
+    _Float16 dd[8][64];                 // d[n][b] * 2^-t_b, [b][n]
+    float tb[8];                        // 2^t_b
+    float inv[16];                      // 2^-e per dY row
+};
+
+// Largest magnitude over the 64 lanes of a wavefront (non-negative values:
+// their bit patterns order as unsigned integers); every lane receives it.
+__device__ __forceinline__ float wave64_max(float f) {
+    uint32_t v = __builtin_bit_cast(uint32_t, row16_max(f));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return __builtin_bit_cast(float, max(max(r0, r1), max(r2, r3)));
+}
+
+// Two codes (bytes 0 and 1 of w, or 2 and 3 when HI) as the f16 pair q - 8:
+// 0x6400 | q is the half 1024 + q.
+template <bool HI>
+__device__ __forceinline__ bv2h codes_m8(uint32_t w) {
+    const uint32_t h = __builtin_amdgcn_perm(0x64646464u, w, HI ? 0x04030402u : 0x04010400u);
+    return __builtin_bit_cast(bv2h, h) - bv2h{(_Float16)1032.0f, (_Float16)1032.0f};
+}
+
+__global__ __launch_bounds__(BT, 2) void backward_q4_0_f16_kernel(int M, int K, int N, int rows_per, int nr,
+                                                                  const uint8_t* __restrict__ w,
+                                                                  const uint16_t* __restrict__ wscale,
+                                                                  const float* __restrict__ dy,
+                                                                  float* __restrict__ work) {
+    __shared__ BwdQ0Lds S[2];  // stage i in S[i & 1]; the next stage's loads wait in registers
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // XCD mapping as in backward_q4k_f16_kernel: the 16 columns of one (row
+    // range, dY tile) share cache lines of the same rows and run on one XCD
+    const int nkb = K / KCOL, ngrp = nr * (int)((M + 15) / 16);
+    const int b = blockIdx.x, xcd = b & 7, t8 = b >> 3;
+    const int grp = (t8 / nkb) * 8 + xcd, kb = t8 % nkb;
+    if (grp >= ngrp) return;  // padding of the grid to whole rounds of 8
+    const int nc = grp % nr, m0 = (grp / nr) * 16;
+    const int nbeg = nc * rows_per, nend = min(N, nbeg + rows_per);
+    const int nst = nend > nbeg ? (nend - nbeg + RC - 1) / RC : 0;  // 64-row stages of the range
+    const int ng = K / 32;
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(w, (uint32_t)((size_t)N * (K / 2)));
+    const __amdgpu_buffer_rsrc_t r_s = rsrc(wscale, (uint32_t)((size_t)N * ng * 2));
+    const __amdgpu_buffer_rsrc_t r_dy = rsrc(dy, (uint32_t)((size_t)M * N * 4));
+
+    // staging roles of a thread within a 64-row stage
+    const int crg = tid >> 4, cbg = tid & 15;      // codes: rows 4 crg .. + 3, bytes 8 cbg .. + 7
+    const int hn = lane, hp = wave;                // scales: row hn, blocks 2 hp, 2 hp + 1
+    const int am = tid >> 4, an = 4 * (tid & 15);  // A operands: dY row am, weight rows an .. an + 3
+
+    uint2 rc[4];
+    uint32_t rd[2];
+    float rdy[4];
+    // offsets selected against the out-of-range offset with a bit operation
+    // (no branch around a load, so no wait at a join)
+    auto sel = [](uint32_t o, bool in) { return o | ((uint32_t)!in << 31); };
+    const uint32_t rowb = (uint32_t)(K / 2), colb = (uint32_t)kb * 128u;
+    const bool dyok = m0 + am < M;
+    const uint32_t dyrow = (uint32_t)(m0 + am) * (uint32_t)N * 4u;
+    auto load = [&](int r0) {  // rows past the range read zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = r0 + 4 * crg + i;
+            rc[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                  r_w, sel((uint32_t)n * rowb + colb + 8u * (uint32_t)cbg, n < nend),
+                                                  0, 0));
+        }
+        {
+            const int n = r0 + hn;
+            const uint32_t o = sel(2u * ((uint32_t)n * (uint32_t)ng + 8u * (uint32_t)kb + 2u * (uint32_t)hp), n < nend);
+            rd[0] = __builtin_amdgcn_raw_buffer_load_b16(r_s, o, 0, 0);
+            rd[1] = __builtin_amdgcn_raw_buffer_load_b16(r_s, o + 2u, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = r0 + an + i;
+            rdy[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   r_dy, sel(dyrow + 4u * (uint32_t)n, n < nend && dyok), 0, 0));
+        }
+    };
+    auto store = [&](BwdQ0Lds& T) {
+        // codes: byte b of rows 4 crg .. + 3 into one dword of T.codes[8 cbg + b]
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+            const uint32_t w0 = hw ? rc[0].y : rc[0].x, w1 = hw ? rc[1].y : rc[1].x;
+            const uint32_t w2 = hw ? rc[2].y : rc[2].x, w3 = hw ? rc[3].y : rc[3].x;
+            const uint32_t t01a = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+            const uint32_t t01b = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+            const uint32_t t23a = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+            const uint32_t t23b = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+            const int j0 = 8 * cbg + 4 * hw;
+            *reinterpret_cast<uint32_t*>(&T.codes[j0][4 * crg]) = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(&T.codes[j0 + 1][4 * crg]) = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
+            *reinterpret_cast<uint32_t*>(&T.codes[j0 + 2][4 * crg]) = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
+            *reinterpret_cast<uint32_t*>(&T.codes[j0 + 3][4 * crg]) = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
+        }
+        // block columns 2 hp, 2 hp + 1: the stage's largest |d| of each (this
+        // wavefront's 64 lanes are the 64 rows) into [2^10, 2^11)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float dv = half_to_float(rd[i]);
+            const float mx = wave64_max(fabsf(dv));
+            const int E = (int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF) - 127;  // mx = 1.f * 2^E
+            const int t = max(E - 10, -100);  // an all-zero column keeps finite scales
+            const float down = __builtin_bit_cast(float, (uint32_t)(127 - t) << 23);
+            T.dd[2 * hp + i][hn] = (_Float16)(dv * down);
+            if (lane == 0) T.tb[2 * hp + i] = __builtin_bit_cast(float, (uint32_t)(127 + t) << 23);
+        }
+        // A operands of dY row am and weight rows an .. an + 3
+        {
+            float mx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(rdy[i]));
+            mx = row16_max(mx);  // the 16 threads of dY row am form one DPP row
+            const int E = max((int)((__builtin_bit_cast(uint32_t, mx) >> 23) & 0xFF) - 126, -111);
+            const float sc = __builtin_bit_cast(float, (uint32_t)(127 + 15 - E) << 23);
+            if ((tid & 15) == 0) T.inv[am] = __builtin_bit_cast(float, (uint32_t)(127 - 15 + E) << 23);
+            bv4h ah, al;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float xa = rdy[i] * sc;
+                ah[i] = (_Float16)xa;
+                al[i] = (_Float16)(xa - (float)ah[i]);
+            }
+            *reinterpret_cast<bv4h*>(&T.ahi[am][an]) = ah;
+            *reinterpret_cast<bv4h*>(&T.alo[am][an]) = al;
+        }
+    };
+
+    // wavefront w owns blocks 2w and 2w + 1 of the column: k = 64w + 32bb + 16h
+    // + col for block 2w + bb and nibble plane h (bytes 16 (2w + bb) + col);
+    // tile t = 2 bb + h
+    const int c = wave, g = lane >> 4, col = lane & 15;
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (nst > 0) {
+        load(nbeg);
+        store(S[0]);
+        load(nbeg + RC);
+    }
+    auto do_stage = [&](int i, auto par) {
+        constexpr int P = decltype(par)::value;  // i & 1
+        __syncthreads();  // stage i is in S[P]; every wavefront is done with S[P ^ 1]
+        if (i + 1 < nst) store(S[P ^ 1]);
+        load(nbeg + (i + 2) * RC);
+        const BwdQ0Lds& T = S[P];
+        v4f D[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) D[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int step = 0; step < 2; ++step) {
+            const int nb = 32 * step + 8 * g;  // this lane's 8 weight rows of the 32-row step
+            const bv8h Ahi = *reinterpret_cast<const bv8h*>(&T.ahi[col][nb]);
+            const bv8h Alo = *reinterpret_cast<const bv8h*>(&T.alo[col][nb]);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int blk = 2 * c + bb;
+                const uint2 cb = *reinterpret_cast<const uint2*>(&T.codes[16 * blk + col][nb]);
+                const uint4 dq = *reinterpret_cast<const uint4*>(&T.dd[blk][nb]);
+                const bv2h d2[4] = {__builtin_bit_cast(bv2h, dq.x), __builtin_bit_cast(bv2h, dq.y),
+                                    __builtin_bit_cast(bv2h, dq.z), __builtin_bit_cast(bv2h, dq.w)};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t w0 = h ? (cb.x >> 4) & 0x0F0F0F0Fu : cb.x & 0x0F0F0F0Fu;
+                    const uint32_t w1 = h ? (cb.y >> 4) & 0x0F0F0F0Fu : cb.y & 0x0F0F0F0Fu;
+                    const bv2h q2[4] = {codes_m8<false>(w0), codes_m8<true>(w0), codes_m8<false>(w1), codes_m8<true>(w1)};
+                    bv8h Bhi, Blo;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const bv2h hi = d2[p] * q2[p];
+                        const bv2h lo = __builtin_elementwise_fma(d2[p], q2[p], -hi);
+                        Bhi[2 * p] = hi[0], Bhi[2 * p + 1] = hi[1];
+                        Blo[2 * p] = lo[0], Blo[2 * p + 1] = lo[1];
+                    }
+                    const int t = 2 * bb + h;
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Bhi, D[t], 0, 0, 0);
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, Blo, D[t], 0, 0, 0);
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Bhi, D[t], 0, 0, 0);
+                    D[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, Blo, D[t], 0, 0, 0);
+                }
+            }
+        }
+        // D layout: lane (col, g) holds rows 4g .. 4g + 3 of column col
+        const v4f iv = *reinterpret_cast<const v4f*>(&T.inv[4 * g]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float up = T.tb[2 * c + (t >> 1)];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(iv[r] * up, D[t][r], acc[t][r]);
+        }
+    };
+    int i = 0;
+    for (; i + 1 < nst; i += 2) {
+        do_stage(i, std::integral_constant<int, 0>());
+        do_stage(i + 1, std::integral_constant<int, 1>());
+    }
+    if (i < nst) do_stage(i, std::integral_constant<int, 0>());
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int k = kb * KCOL + 64 * c + 32 * (t >> 1) + 16 * (t & 1) + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = m0 + 4 * g + r;
+            if (m < M) work[((size_t)nc * M + m) * K + k] = acc[t][r];
+        }
+    }
+}
+
 // dx[m][k] = sum over ranges c of work[c][m][k] in a fixed order: a workgroup
 // of 8 wavefronts takes 64 consecutive outputs; wavefront w sums ranges
 // w, w + 8, w + 16, ... in order (loads issued 16 at a time), and the eight
@@ -695,11 +919,15 @@ hipError_t launch_b(int M, int K, int N, const uint8_t* w, const void* ws, const
     const int nr = backward_ranges(M, K, N);
     const int rows_per = (N + nr - 1) / nr;
     const dim3 grid(K / KCOL, nr, (M + 15) / 16);
-    if (FMTB == 2) {
+    if (FMTB == 2 || FMTB == 0) {
         const long long ngrp = (long long)nr * ((M + 15) / 16);
         const unsigned nwg = (unsigned)(((ngrp + 7) / 8) * 8 * (K / KCOL));
-        hipLaunchKernelGGL(backward_q4k_f16_kernel, dim3(nwg), dim3(BT), 0, stream, M, K, N, rows_per, nr, w, dy,
-                           work);
+        if (FMTB == 2)
+            hipLaunchKernelGGL(backward_q4k_f16_kernel, dim3(nwg), dim3(BT), 0, stream, M, K, N, rows_per, nr, w, dy,
+                               work);
+        else
+            hipLaunchKernelGGL(backward_q4_0_f16_kernel, dim3(nwg), dim3(BT), 0, stream, M, K, N, rows_per, nr, w,
+                               static_cast<const uint16_t*>(ws), dy, work);
     } else
         hipLaunchKernelGGL((backward_partial_kernel<FMTB, G>), grid, dim3(BT), 0, stream, M, K, N, rows_per, w,
                            static_cast<const uint16_t*>(ws), static_cast<const uint16_t*>(wb), dy, work);

@@ -676,6 +676,48 @@ def test_q4k_backward_workload(M):
     assert abs(lhs - rhs) <= 1e-4 * np.sqrt(M * wl.N) * np.abs(to_np(y)).mean()
 
 
+@pytest.mark.parametrize("M", [16, 40])
+def test_q4_backward_workload(M):
+    # the Q4_K workload's weights (N=14336, K=4096) quantized as Q4_0; above 4 dY
+    # rows the f16 matrix-core kernel (hi/lo halves of dY and of d * (q - 8))
+    print(f"case q4_0 backward workload M={M}", flush=True)
+    wl = synth.workload("q4_k_gemv_1x4096x14336")
+    wts = oracle.quantize_q4_0(synth.gen.weights(wl))
+    dy = np.random.default_rng(5151 + M).standard_normal((M, wl.N)).astype(np.float32)
+    g = _wts_dev("q4_0", wts)
+    gdy = to_dev(dy)
+    dx = q4.gemm_backward("q4_0", 32, *g, gdy)
+    dx2 = q4.gemm_backward("q4_0", 32, *g, gdy)
+    _sync()
+    assert torch.equal(dx, dx2)
+    ms, ks = sample_pairs(M, wl.K, 400, 31 + M)
+    ref = oracle.q4_backward_sample(wts[0], wts[1], None, dy, wl.K, wl.N, 32, FMT["q4_0"], ms, ks)
+    assert rel_rms(to_np(dx)[ms, ks], ref) <= TOL
+
+
+def test_q4_backward_scale_extremes():
+    # Q4_0 block scales from about 1e-4 to 6e4 in one weight matrix: every
+    # block column of the f16 kernel is brought to its own range, so the large
+    # scales do not overflow f16 and the small ones keep their precision
+    print("case q4_0 backward scale extremes", flush=True)
+    M, K, N = 16, 512, 200
+    rng = np.random.default_rng(77)
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    w[::7] *= np.float32(2e6)     # d up to about 6e4 (beyond 65504 / 8)
+    w[3::11] *= np.float32(1e-2)  # d about 1e-4
+    w[:, 64:96] *= np.float32(1e-3)  # one block column much smaller than the rest
+    wts = oracle.quantize_q4_0(w)
+    assert np.abs(wts[1].view(np.float16).astype(np.float32)).max() > 8192
+    dy = rng.standard_normal((M, N)).astype(np.float32)
+    dx = q4.gemm_backward("q4_0", 32, *_wts_dev("q4_0", wts), to_dev(dy))
+    _sync()
+    got = to_np(dx)
+    ref = oracle.q4_backward(wts[0], wts[1], None, dy, K, N, 32, FMT["q4_0"])
+    assert np.all(np.isfinite(got))
+    assert rel_rms(got, ref) <= TOL
+    assert rel_rms(got[:, 64:96], ref[:, 64:96]) <= TOL
+
+
 def test_q4_backward_decode_workload_sampled():
     print("case backward q4_0 decode weights M=4", flush=True)
     wl, _, _, _, wts = workload_data("q4_0_decode_4096")
