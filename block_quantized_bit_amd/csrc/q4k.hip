@@ -302,12 +302,14 @@ __device__ __forceinline__ void codes_f16(uint2 cw, v8h& blo, v8h& bhi) {
 // per-row sub-block sums and the row's 2^-e. Lane l of a wavefront holds
 // weight row l % 16; its operands for k = 8 (l / 16) .. +7 of a sub-block are 8
 // bytes of qs (low nibbles: sub-block 2c, high nibbles: 2c + 1, chunk c), so
-// one sub-block is two MFMAs (hi, lo). The next super-block's loads are in
-// registers while the current one is computed, and the staged tiles are
-// double-buffered, so a super-block costs one barrier. All loads are buffer
+// one sub-block is two MFMAs (hi, lo). The loads of the next D super-blocks
+// are in registers while the current one is computed (each slot's registers
+// are refilled in place, after their last use, so no register copy waits for
+// a load in flight), and the staged tiles are double-buffered, so a
+// super-block costs one barrier. All loads are buffer
 // loads with no branch around them: rows past M or N and super-blocks past a
 // range read zero.
-constexpr int XR = QK + 8;  // halves per staged row: 16-byte aligned, rows 4 banks apart
+constexpr int XR = QK + 16;  // halves per staged row: 544 bytes, no LDS bank conflicts on the A-operand reads (measured; 528 bytes gave 31%)
 
 template <int W, int KP>
 struct Q4kStage {
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(256) void q4k_split_kernel(int M, int K, const floa
     if (c4 == 0) inv[r] = ivs;
 }
 
-template <int W, int KP, bool PRESPLIT>
+template <int W, int KP, bool PRESPLIT, int D>
 __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int N, const uint8_t* __restrict__ blocks,
                                                                const float* __restrict__ x, float* __restrict__ y,
                                                                const uint8_t* __restrict__ work) {
@@ -365,6 +367,7 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
     static_assert(XCH * NTH == 16 * QK / 4, "staging covers the tile");
     constexpr int UPT = 1024 / NTH;         // PRESPLIT: hi / lo units of the split tile per thread
     static_assert(UPT * NTH == 1024 && NTH >= 36, "the split tile is copied as UPT + 1 units per thread");
+    static_assert(D >= 2, "the loads of the next super-block's tile are staged one iteration ahead");
     __shared__ Q4kStage<W, KP> st[KP];
     // the wavefront index is uniform: the K range, and with it every load's scalar offset, stays in SGPRs
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -385,59 +388,69 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
         ox[i] = (m0 + r < M) ? (uint32_t)(((size_t)(m0 + r) * K + 4 * c4) * 4) : OUT;
     }
     const uint32_t ow = (n < N) ? (uint32_t)((size_t)n * nsb * BLOCK_BYTES) : OUT;
-
-    float4 rx[XCH];
-    uint4 ru[UPT], ru5;  // PRESPLIT: the tile's 16-byte units tp + NTH i, and unit 1024 + tp (tp < 36)
     const __amdgpu_buffer_rsrc_t r_t =
         rsrc(work, PRESPLIT ? (uint32_t)((size_t)((M + 15) / 16) * nsb * TILE_UNITS * 16) : 0u);
     const uint32_t otile = (uint32_t)((size_t)blockIdx.y * nsb * TILE_UNITS * 16);
-    uint4 rh;
-    uint2 rq[4];
-    auto load = [&](int sb) {  // super-blocks past the range read zero
+
+    // The loads of one super-block: the activation tile (PRESPLIT: the split
+    // tile's 16-byte units tp + NTH i, and unit 1024 + tp for tp < 36) and the
+    // lane's weight header and code bytes. D of them are in flight: the
+    // super-block sb's are issued D iterations before its arithmetic.
+    struct Slot {
+        float4 rx[PRESPLIT ? 1 : XCH];
+        uint4 ru[PRESPLIT ? UPT : 1], ru5;
+        uint4 rh;
+        uint2 rq[4];
+    };
+    Slot sl[D];
+    auto load_x = [&](Slot& L, int sb) {  // super-blocks past the range read zero
         const bool in = sb < sb1;
         if (PRESPLIT) {
             const uint32_t so = in ? otile + (uint32_t)sb * TILE_UNITS * 16 : 0u;
 #pragma unroll
             for (int i = 0; i < UPT; ++i)
-                ru[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      r_t, in ? (uint32_t)(tp + NTH * i) * 16 : OUT, so, 0));
-            ru5 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                r_t, (in && tp < 36) ? (uint32_t)(1024 + tp) * 16 : OUT, so, 0));
+                L.ru[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        r_t, in ? (uint32_t)(tp + NTH * i) * 16 : OUT, so, 0));
+            L.ru5 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  r_t, (in && tp < 36) ? (uint32_t)(1024 + tp) * 16 : OUT, so, 0));
         } else {
 #pragma unroll
             for (int i = 0; i < XCH; ++i)
-                rx[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? ox[i] : OUT,
-                                                                                         in ? sb * QK * 4 : 0, 0));
+                L.rx[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r_x, in ? ox[i] : OUT,
+                                                                                           in ? sb * QK * 4 : 0, 0));
         }
+    };
+    auto load_w = [&](Slot& L, int sb) {
+        const bool in = sb < sb1;
         const uint32_t o = in ? ow : OUT, so = in ? (uint32_t)(sb * BLOCK_BYTES) : 0u;
-        rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, so, 0));
+        L.rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, so, 0));
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            rq[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                  r_w, o == OUT ? OUT : o + 16 + 32 * c + 8 * q, so, 0));
+            L.rq[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                    r_w, o == OUT ? OUT : o + 16 + 32 * c + 8 * q, so, 0));
     };
     // Stage the tile in buffer b: row r = wave-in-group + W i is held by the 64
     // lanes of one wavefront (lane = float4 index), so its largest magnitude
     // and its sub-block sums are wavefront and 8-lane reductions.
-    auto stage = [&](int b) {
+    auto stage = [&](int b, const Slot& L) {
         Q4kStage<W, KP>& S = st[p];
         if (PRESPLIT) {  // a copy of the split tile into the padded LDS rows
 #pragma unroll
             for (int i = 0; i < UPT; ++i) {
                 const int u = tp + NTH * i, half = u >> 9, r = (u >> 5) & 15, c8 = u & 31;
                 v8h* dst = half ? S.lo[b] : S.hi[b];
-                dst[r * (XR / 8) + c8] = __builtin_bit_cast(v8h, ru[i]);
+                dst[r * (XR / 8) + c8] = __builtin_bit_cast(v8h, L.ru[i]);
             }
             if (tp < 32)
-                *reinterpret_cast<uint4*>(&S.sum[b][0][0] + 4 * tp) = ru5;
+                *reinterpret_cast<uint4*>(&S.sum[b][0][0] + 4 * tp) = L.ru5;
             else if (tp < 36)
-                *reinterpret_cast<uint4*>(&S.inv[b][4 * (tp - 32)]) = ru5;
+                *reinterpret_cast<uint4*>(&S.inv[b][4 * (tp - 32)]) = L.ru5;
             return;
         }
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int idx = tp + NTH * i, r = idx >> 6, c4 = idx & 63;
-            const float4 v = rx[i];
+            const float4 v = L.rx[i];
             float sc, ivs;
             split_scale(v, sc, ivs);
             const float xs0 = v.x * sc, xs1 = v.y * sc, xs2 = v.z * sc, xs3 = v.w * sc;
@@ -454,54 +467,63 @@ __global__ __launch_bounds__(64 * W * KP) void q4k_gemm_kernel(int M, int K, int
     };
 
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    load(sb0);
-    stage(0);
-    uint4 hdr = rh;
-    uint2 cw[4] = {rq[0], rq[1], rq[2], rq[3]};
-    load(sb0 + 1);
+#pragma unroll
+    for (int s2 = 0; s2 < D; ++s2) {
+        load_x(sl[s2], sb0 + s2);
+        load_w(sl[s2], sb0 + s2);
+    }
+    stage(0, sl[0]);
     const int row = lane & 15;  // activation row of this lane's A operands
-    for (int it = 0; it < per; ++it) {  // the same trip count in every range (past its end: zeros)
-        const int sb = sb0 + it;
-        __syncthreads();  // tile it is complete; every wavefront is done with the other buffer
-        stage((it + 1) & 1);
-        const uint4 ch = hdr;
-        const uint2 c0 = cw[0], c1 = cw[1], c2 = cw[2], c3 = cw[3];
-        hdr = rh;
+    // The same trip count in every range (past its end: zeros). Iteration it
+    // stages the tile of super-block it + 1 from its slot, refills the tile
+    // part of its own slot (staged one iteration earlier) with super-block
+    // it + D, computes super-block it from the weights in its slot and then
+    // refills them too; the slot registers are used in place, so no register
+    // copy waits for a load in flight.
+    for (int it0 = 0; it0 < per; it0 += D) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) cw[c] = rq[c];
-        load(sb + 2);
-        const int b = it & 1;
-        const Q4kStage<W, KP>& S = st[p];
-        const float d = half_to_float(ch.x & 0xFFFFu), dmin = half_to_float(ch.x >> 16);
-        const uint2 cc[4] = {c0, c1, c2, c3};
-        v4f part = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int u = 0; u < D; ++u) {
+            const int it = it0 + u;
+            if (it >= per) break;
+            const int sb = sb0 + it;
+            __syncthreads();  // tile it is complete; every wavefront is done with the other buffer
+            stage((it + 1) & 1, sl[(u + 1) % D]);
+            load_x(sl[u], sb + D);
+            const uint4 ch = sl[u].rh;
+            const uint2* cc = sl[u].rq;
+            const int b = it & 1;
+            const Q4kStage<W, KP>& S = st[p];
+            const float d = half_to_float(ch.x & 0xFFFFu), dmin = half_to_float(ch.x >> 16);
+            v4f part = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float sc0, sc1, mm0, mm1;
-            q4k_pair_scales(ch, c, sc0, sc1, mm0, mm1);
-            v8h blo, bhi;
-            codes_f16(cc[c], blo, bhi);
-            const v8h* H = S.hi[b] + (row * XR + 64 * c + 8 * q) / 8;
-            const v8h* L = S.lo[b] + (row * XR + 64 * c + 8 * q) / 8;
-            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-            v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(H[0], blo, z, 0, 0, 0);
-            d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(L[0], blo, d0, 0, 0, 0);
-            v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(H[4], bhi, z, 0, 0, 0);  // k + 32: sub-block 2c + 1
-            d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(L[4], bhi, d1, 0, 0, 0);
-            const v4f s0 = *reinterpret_cast<const v4f*>(&S.sum[b][2 * c][4 * q]);
-            const v4f s1 = *reinterpret_cast<const v4f*>(&S.sum[b][2 * c + 1][4 * q]);
-            const float a0 = d * sc0, a1 = d * sc1, e0 = dmin * mm0, e1 = dmin * mm1;
+            for (int c = 0; c < 4; ++c) {
+                float sc0, sc1, mm0, mm1;
+                q4k_pair_scales(ch, c, sc0, sc1, mm0, mm1);
+                v8h blo, bhi;
+                codes_f16(cc[c], blo, bhi);
+                const v8h* H = S.hi[b] + (row * XR + 64 * c + 8 * q) / 8;
+                const v8h* L = S.lo[b] + (row * XR + 64 * c + 8 * q) / 8;
+                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                v4f d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(H[0], blo, z, 0, 0, 0);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(L[0], blo, d0, 0, 0, 0);
+                v4f d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(H[4], bhi, z, 0, 0, 0);  // k + 32: sub-block 2c + 1
+                d1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(L[4], bhi, d1, 0, 0, 0);
+                const v4f s0 = *reinterpret_cast<const v4f*>(&S.sum[b][2 * c][4 * q]);
+                const v4f s1 = *reinterpret_cast<const v4f*>(&S.sum[b][2 * c + 1][4 * q]);
+                const float a0 = d * sc0, a1 = d * sc1, e0 = dmin * mm0, e1 = dmin * mm1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                part[r] = fmaf(a0, d0[r], part[r]);
-                part[r] = fmaf(-e0, s0[r], part[r]);
-                part[r] = fmaf(a1, d1[r], part[r]);
-                part[r] = fmaf(-e1, s1[r], part[r]);
+                for (int r = 0; r < 4; ++r) {
+                    part[r] = fmaf(a0, d0[r], part[r]);
+                    part[r] = fmaf(-e0, s0[r], part[r]);
+                    part[r] = fmaf(a1, d1[r], part[r]);
+                    part[r] = fmaf(-e1, s1[r], part[r]);
+                }
             }
-        }
-        const v4f iv = *reinterpret_cast<const v4f*>(&S.inv[b][4 * q]);
+            const v4f iv = *reinterpret_cast<const v4f*>(&S.inv[b][4 * q]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = fmaf(iv[r], part[r], acc[r]);
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(iv[r], part[r], acc[r]);
+            load_w(sl[u], sb + D);
+        }
     }
     // add the K ranges in order (p = 0, 1, ...) through LDS, reusing the staging memory
     if (KP > 1) {
@@ -560,11 +582,17 @@ hipError_t launch_q4k_gemv(int K, int N, const void* blocks, const float* x, flo
     return hipGetLastError();
 }
 
+// Super-blocks of loads in flight per wavefront. Measured at 16 x 4096 x 14336
+// (cold weights): 2: 22.6 / 20.8 us (q4k_gemm / with the split), 3: 24.5 / 23.0,
+// 4: 26.2 / 23.1; with the loop fully unrolled (exact load waits) 3 and 4 were
+// still slower than 2.
+constexpr int QD = 2;
+
 hipError_t launch_q4k_gemm(int M, int K, int N, const void* blocks, const float* x, float* y, hipStream_t stream) {
     constexpr int W = 4;   // wavefronts (16 weight rows each) per K range
     constexpr int KP = 2;  // K ranges per workgroup (1: 34.3 us, 2: 29.5, 4: 30.0 at 16 x 4096 x 14336)
     const dim3 grid((unsigned)((N + 16 * W - 1) / (16 * W)), (unsigned)((M + 15) / 16));
-    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP, false>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
+    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP, false, QD>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
                        static_cast<const uint8_t*>(blocks), x, y, nullptr);
     return hipGetLastError();
 }
@@ -575,7 +603,7 @@ template <int W, int KP>
 hipError_t launch_presplit(int M, int K, int N, const void* blocks, const float* x, float* y, const uint8_t* wk,
                            hipStream_t stream) {
     const dim3 grid((unsigned)((N + 16 * W - 1) / (16 * W)), (unsigned)((M + 15) / 16));
-    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP, true>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
+    hipLaunchKernelGGL((q4k_gemm_kernel<W, KP, true, QD>), grid, dim3(64 * W * KP), 0, stream, M, K, N,
                        static_cast<const uint8_t*>(blocks), x, y, wk);
     return hipGetLastError();
 }
