@@ -259,25 +259,26 @@ __device__ __forceinline__ void split_scale(const float4& v, float& sc, float& i
     inv = __builtin_bit_cast(float, (uint32_t)(127 - 15 + E) << 23);
 }
 
-// Two codes (nibbles in bits 0..3 and 16..19 of t) as an exact f16 pair:
-// 0x6400 | q is the half 1024 + q, and subtracting 1024 leaves q.
-__device__ __forceinline__ uint32_t code_pair_f16(uint32_t t) {
-    v2h h = __builtin_bit_cast(v2h, (t & 0x000F000Fu) | 0x64006400u);
+// Bytes 0 and 1 (SEL01) or 2 and 3 (SEL23) of a word of isolated nibbles as
+// an exact f16 pair: v_perm places each code byte under the byte 0x64, giving
+// the half 0x6400 | q = 1024 + q, and subtracting 1024 leaves q.
+constexpr uint32_t SEL01 = 0x04010400u, SEL23 = 0x04030402u;
+__device__ __forceinline__ uint32_t code_pair_f16(uint32_t nib, uint32_t sel) {
+    v2h h = __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, nib, sel));
     h = h - v2h{(_Float16)1024.0f, (_Float16)1024.0f};
     return __builtin_bit_cast(uint32_t, h);
 }
 
 // The 16 codes of 8 qs bytes as two f16 MFMA operands: low nibbles (byte i is
 // weight k = i of the lane's 8 in one sub-block) and high nibbles (the same k
-// in the next sub-block).
+// in the next sub-block). 22 instructions for 16 codes.
 __device__ __forceinline__ void codes_f16(uint2 cw, v8h& blo, v8h& bhi) {
-    const uint32_t p0 = __builtin_amdgcn_perm(0u, cw.x, 0x0C010C00u);  // bytes 0, 1 into the two halves
-    const uint32_t p1 = __builtin_amdgcn_perm(0u, cw.x, 0x0C030C02u);  // bytes 2, 3
-    const uint32_t p2 = __builtin_amdgcn_perm(0u, cw.y, 0x0C010C00u);
-    const uint32_t p3 = __builtin_amdgcn_perm(0u, cw.y, 0x0C030C02u);
-    blo = __builtin_bit_cast(v8h, make_uint4(code_pair_f16(p0), code_pair_f16(p1), code_pair_f16(p2), code_pair_f16(p3)));
-    bhi = __builtin_bit_cast(v8h, make_uint4(code_pair_f16(p0 >> 4), code_pair_f16(p1 >> 4), code_pair_f16(p2 >> 4),
-                                             code_pair_f16(p3 >> 4)));
+    const uint32_t lx = cw.x & 0x0F0F0F0Fu, ly = cw.y & 0x0F0F0F0Fu;
+    const uint32_t hx = (cw.x >> 4) & 0x0F0F0F0Fu, hy = (cw.y >> 4) & 0x0F0F0F0Fu;
+    blo = __builtin_bit_cast(v8h, make_uint4(code_pair_f16(lx, SEL01), code_pair_f16(lx, SEL23),
+                                             code_pair_f16(ly, SEL01), code_pair_f16(ly, SEL23)));
+    bhi = __builtin_bit_cast(v8h, make_uint4(code_pair_f16(hx, SEL01), code_pair_f16(hx, SEL23),
+                                             code_pair_f16(hy, SEL01), code_pair_f16(hy, SEL23)));
 }
 
 // GEMM on the f16 matrix cores (v_mfma_f32_16x16x32_f16), float32-accurate.
