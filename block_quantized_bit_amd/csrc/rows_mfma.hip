@@ -8,10 +8,11 @@
 // stays bound by its weight stream, a few more activation rows should cost
 // little more time than one.
 //
-// Mapping. A workgroup of 16 wavefronts owns 16 consecutive weight rows. The
-// blocks of a row are taken four at a time (a "quad": 128 weights, 64 bytes of
-// codes per row) and the wavefronts take the quads round-robin, so the
-// workgroup's loads in flight cover a contiguous stretch of every row. In a
+// Mapping. A workgroup of 16 wavefronts (8 for 17..32 rows) owns 16
+// consecutive weight rows. The blocks of a row are taken four at a time (a
+// "quad": 128 weights, 64 bytes of codes per row) and the wavefronts take the
+// quads round-robin, so the workgroup's loads in flight cover a contiguous
+// stretch of every row. In a
 // wavefront, lane (q, c) = (l / 16, l % 16) loads block 4j + q of weight row c
 // (one 128-bit load) and the 32 activation codes of block 4j + q of activation
 // row c of each 16-row tile (two). A 4x4 transpose of dwords across the four
@@ -45,8 +46,11 @@ namespace q4 {
 
 namespace {
 
-constexpr int RW = 16;          // wavefronts per workgroup
-constexpr int RNT = 64 * RW;    // threads per workgroup
+// Wavefronts per workgroup: 16 for one 16-row activation tile, 8 for two
+// (measured, Q4_0 24 and 32 rows: 4096 x 14336 24.9 -> 21.9 us and 27.9 ->
+// 25.3 us, 14336 x 4096 21.6 -> 20.9 and 24.7 -> 24.2, 4096 x 4096 within
+// 2%; with 3..16 rows 8 wavefronts were up to 6% slower)
+constexpr int rows_waves(int mt) { return mt == 1 ? 16 : 8; }
 constexpr int RN = 16;          // weight rows per workgroup
 constexpr int RSRC_WORD3 = 0x00020000;
 constexpr uint32_t OUT = 0x80000000u;  // beyond every buffer range: reads as zero
@@ -98,7 +102,9 @@ struct Quad {
 // wavefronts' float tiles for the final sum.
 constexpr int wave_lds_bytes(int fmt, int mt) { return (fmt == 1 ? 2 : 1) * (4 * 16 * mt * 4 + 16 * 4 * 2); }
 
-size_t rows_mfma_lds(int fmt, int mt) { return (size_t)RW * wave_lds_bytes(fmt, mt) + (size_t)RW * mt * 256 * 4; }
+size_t rows_mfma_lds(int fmt, int mt) {
+    return (size_t)rows_waves(mt) * wave_lds_bytes(fmt, mt) + (size_t)rows_waves(mt) * mt * 256 * 4;
+}
 
 // DEPTH: quads in flight per wavefront (2, or 4 for long rows). With one
 // 16-row tile and two quads in flight the kernel fits 64 registers, so two
@@ -108,7 +114,7 @@ size_t rows_mfma_lds(int fmt, int mt) { return (size_t)RW * wave_lds_bytes(fmt, 
 // the second half of row c's block; after the transpose a DPP row rotation by
 // 8 lanes hands each lane c < 8 its second-half dwords.
 template <int FMT, int G, int MT, bool PARTIALS, int DEPTH, bool HALF>
-__global__ __launch_bounds__(RNT, (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 64)) ? 8 : 4) void rows_mfma_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
+__global__ __launch_bounds__(64 * rows_waves(MT), (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 64)) ? 8 : 4) void rows_mfma_kernel(int M, int K, int N, const uint8_t* __restrict__ wq,
                                                        const uint16_t* __restrict__ wscale,
                                                        const uint16_t* __restrict__ wbias,
                                                        const int8_t* __restrict__ xq, const float* __restrict__ xs,
@@ -116,6 +122,7 @@ __global__ __launch_bounds__(RNT, (MT == 1 && DEPTH == 2 && !(FMT == 1 && G == 6
                                                        int32_t* __restrict__ partials) {
     constexpr bool AFF = FMT == 1;
     constexpr int MR = 16 * MT;
+    constexpr int RW = rows_waves(MT), RNT = 64 * RW;
     static_assert(!HALF || MT == 1, "the half tile is one 16-row tile");
     using Q = Quad<MT>;
     constexpr int SPG = G / 32;   // blocks per group
@@ -341,6 +348,7 @@ hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale,
     // one 16-row tile: four quads in flight once a wavefront has at least four
     // to do; up to 8 rows: the half tile
     constexpr int DEEP = MT == 1 ? 4 : 2;
+    constexpr int RW = rows_waves(MT);
     const bool deep = (K / 128) >= 4 * RW;
     decltype(&rows_mfma_kernel<FMT, G, MT, true, 2, false>) k;
     if (MT == 1 && M <= 8)
@@ -355,7 +363,7 @@ hipError_t launch_mt(int M, int K, int N, const uint8_t* wq, const void* wscale,
         const hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(k), lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k, dim3((unsigned)((N + RN - 1) / RN)), dim3(RNT), lds, stream, M, K, N, wq,
+    hipLaunchKernelGGL(k, dim3((unsigned)((N + RN - 1) / RN)), dim3(64 * RW), lds, stream, M, K, N, wq,
                        static_cast<const uint16_t*>(wscale), static_cast<const uint16_t*>(wbias), xq, xs, xsum, y,
                        partials);
     return hipGetLastError();
