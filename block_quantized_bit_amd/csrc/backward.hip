@@ -35,6 +35,10 @@ constexpr int RC = 64;        // weight rows per LDS stage
 constexpr int Q4K_BYTES = 144;
 constexpr int RSRC_WORD3 = 0x00020000;
 constexpr uint32_t OUT = 0x80000000u;
+// Offset o where `in`, else o with bit 31 set (past every buffer range: reads
+// zero). A bit operation rather than a select: with a condition the compiler
+// can branch around the load and wait for every load in flight at the join.
+__device__ __forceinline__ uint32_t sel(uint32_t o, bool in) { return o | ((uint32_t)!in << 31); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, RSRC_WORD3);
@@ -116,16 +120,16 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
         const bool in = n < nend;
         uint32_t o = OUT;
         if (FMTB == 2) {
-            o = in ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES + 16 + 32 * part) : OUT;
+            o = sel((uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES + 16 + 32 * part), in);
             rh = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               r_w, in ? (uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES) : OUT, 0, 0));
+                                               r_w, sel((uint32_t)(((size_t)n * (K / 256) + kb) * Q4K_BYTES), in), 0, 0));
         } else {
-            o = in ? (uint32_t)((size_t)n * (K / 2) + (size_t)kb * 128 + 32 * part) : OUT;
+            o = sel((uint32_t)((size_t)n * (K / 2) + (size_t)kb * 128 + 32 * part), in);
             const int g0 = (kb * 256 + 32 * s0) / G, g1 = (kb * 256 + 32 * (s0 + 1)) / G;
             // the group offsets differ between lanes: per-lane offsets (a scalar offset
             // that varies over the wavefront makes the compiler loop over its values)
             const uint32_t ob = (uint32_t)((size_t)n * ngroups * 2);
-            const uint32_t o0 = in ? ob + 2u * g0 : OUT, o1 = in ? ob + 2u * g1 : OUT;
+            const uint32_t o0 = sel(ob + 2u * g0, in), o1 = sel(ob + 2u * g1, in);
             ra0 = __builtin_amdgcn_raw_buffer_load_b16(r_s, o0, 0, 0);
             ra1 = __builtin_amdgcn_raw_buffer_load_b16(r_s, o1, 0, 0);
             rb0 = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, o0, 0, 0) : 0u;
@@ -133,11 +137,11 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
         }
         // Q4_K blocks are 144 bytes: 16-byte aligned offsets (144 = 9 * 16), so 128-bit loads
         rc0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o, 0, 0));
-        rc1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o == OUT ? OUT : o + 16, 0, 0));
+        rc1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, o + 16, 0, 0));  // bit 31 stays set
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int idx = tid + BT * i, m = idx >> 6, r = idx & 63, nn = r0 + r;
-            const uint32_t od = (m0 + m < M && nn < nend) ? (uint32_t)(((size_t)(m0 + m) * N + nn) * 4) : OUT;
+            const uint32_t od = sel((uint32_t)(((size_t)(m0 + m) * N + nn) * 4), m0 + m < M && nn < nend);
             rdy[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_dy, od, 0, 0));
         }
     };
@@ -280,17 +284,17 @@ __global__ __launch_bounds__(64 * RW) void backward_rows_kernel(int M, int K, in
             const int r = r0 + i;
             const bool in = uin && r < nrows;
             const uint32_t rb = (uint32_t)r * rowbytes;
-            P.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, in ? rb + qoff : OUT, 0, 0));
+            P.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, sel(rb + qoff, in), 0, 0));
             if (FMTB == 2) {
-                P.h[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, in ? rb + hoff : OUT, 0, 0));
+                P.h[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r_w, sel(rb + hoff, in), 0, 0));
             } else {
-                const uint32_t so = in ? (uint32_t)r * ngroups * 2u + soff : OUT;
+                const uint32_t so = sel((uint32_t)r * ngroups * 2u + soff, in);
                 P.a[i] = __builtin_amdgcn_raw_buffer_load_b16(r_s, so, 0, 0);
                 P.b[i] = FMTB == 1 ? __builtin_amdgcn_raw_buffer_load_b16(r_b, so, 0, 0) : (uint16_t)0;
             }
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
-                const uint32_t o = (m < M && r < nrows) ? (uint32_t)(((size_t)m * N + n0 + r) * 4) : OUT;
+                const uint32_t o = sel((uint32_t)(((size_t)m * N + n0 + r) * 4), m < M && r < nrows);
                 P.d[i][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_dy, o, 0, 0));
             }
         }
@@ -304,11 +308,10 @@ __global__ __launch_bounds__(64 * RW) void backward_rows_kernel(int M, int K, in
         bs[m][0] = bs[m][1] = 0.0f;
     }
 
-    RowPass<FMTB, MR> cur;
-    load(cur, 0);
-    for (int r0 = 0; r0 < nrows; r0 += RR) {
-        RowPass<FMTB, MR> nxt;
-        if (r0 + RR < nrows) load(nxt, r0 + RR);
+    // Two passes of loads in flight, in two slots that are refilled in place
+    // after their compute (a register copy of loads in flight would wait for
+    // them); no load is issued for passes past the wavefront's rows.
+    auto compute = [&](const RowPass<FMTB, MR>& cur) {
 #pragma unroll
         for (int i = 0; i < RR; ++i) {
             // w = a * q + b for the low-nibble (0) and high-nibble (1) halves of the chunk
@@ -346,7 +349,17 @@ __global__ __launch_bounds__(64 * RW) void backward_rows_kernel(int M, int K, in
                 bs[m][1] = fmaf(dv, b1, bs[m][1]);
             }
         }
-        cur = nxt;
+    };
+    RowPass<FMTB, MR> pa, pb;
+    load(pa, 0);
+    if (RR < nrows) load(pb, RR);
+    for (int r0 = 0; r0 < nrows; r0 += 2 * RR) {
+        compute(pa);
+        if (r0 + 2 * RR < nrows) load(pa, r0 + 2 * RR);
+        if (r0 + RR < nrows) {
+            compute(pb);
+            if (r0 + 3 * RR < nrows) load(pb, r0 + 3 * RR);
+        }
     }
 
     // output column of each accumulator within the slice
@@ -476,7 +489,6 @@ __global__ __launch_bounds__(BT, 2) void backward_q4k_f16_kernel(int M, int K, i
     // (the buffer range check reads zero at offsets of 2^31 and above): with a
     // condition the compiler branches around the load and, at the join, waits
     // for every load in flight, which serialises the prefetch.
-    auto sel = [](uint32_t o, bool in) { return o | ((uint32_t)!in << 31); };
     const uint32_t rowb = (uint32_t)nsb * Q4K_BYTES, colb = (uint32_t)kb * Q4K_BYTES;
     const bool dyok = m0 + am < M;
     const uint32_t dyrow = (uint32_t)(m0 + am) * (uint32_t)N * 4u;
@@ -709,7 +721,6 @@ __global__ __launch_bounds__(BT, 2) void backward_q4_0_f16_kernel(int M, int K, 
     float rdy[4];
     // offsets selected against the out-of-range offset with a bit operation
     // (no branch around a load, so no wait at a join)
-    auto sel = [](uint32_t o, bool in) { return o | ((uint32_t)!in << 31); };
     const uint32_t rowb = (uint32_t)(K / 2), colb = (uint32_t)kb * 128u;
     const bool dyok = m0 + am < M;
     const uint32_t dyrow = (uint32_t)(m0 + am) * (uint32_t)N * 4u;
