@@ -152,9 +152,10 @@ int q4_gemv_fused(int M, int K, int N, int bs, int fmt, int bits, int xdtype, co
  *     chunk unpacked once and dotted (v_dot4) with the codes of every row,
  *     which are held in registers.
  *   3 <= M <= 32 with 4-bit codes: the same kind of weight stream on the
- *     int8 matrix cores: a workgroup of 16 wavefronts owns 16 weight rows,
- *     its wavefronts take 128-weight stretches of them in turn, and each
- *     32-weight block is one 16x16x32 int8 MFMA per 16 activation rows.
+ *     int8 matrix cores: a workgroup of 16 wavefronts (8 above 16 rows) owns
+ *     16 weight rows, its wavefronts take 128-weight stretches of them in
+ *     turn, and each 32-weight block is one 16x16x32 int8 MFMA per 16
+ *     activation rows.
  *     Its float rescale uses the same exponent bias as the tiled kernel
  *     below (|weight scale| < 2^104).
  *   other M <= 32, and 33 <= M <= 64 with N <= 8192: every weight block is
