@@ -626,7 +626,10 @@ def test_gemm_packed_workload_sampled(name):
 
 BWD_SHAPES = [(1, 256, 1), (3, 512, 70), (16, 1024, 129), (17, 768, 200), (33, 256, 64),
               # up to 4 rows: the weight-stream kernel, with two K slices (the second partial) and ragged N
-              (2, 2304, 45), (4, 4352, 19), (1, 4096, 300)]
+              (2, 2304, 45), (4, 4352, 19), (1, 4096, 300),
+              # 3 and 5 passes per wavefront (odd counts: the second load slot's last pass is skipped),
+              # the last pass partly filled
+              (1, 2048, 18000), (3, 2048, 9000), (4, 2048, 17000)]
 
 
 @pytest.mark.parametrize("M,K,N", BWD_SHAPES)
