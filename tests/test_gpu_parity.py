@@ -324,14 +324,13 @@ SMALL_CASES = [("q4_0", 32, 2, 416, 37), ("q4_0", 32, 16, 96, 17), ("q4_0", 32, 
                # ragged last chunk, rows and columns
                ("q4_0", 32, 33, 544, 20), ("q4_0", 32, 64, 1632, 33), ("affine", 64, 48, 1088, 37),
                ("affine", 64, 64, 4096, 17), ("affine", 128, 40, 2176, 70), ("affine", 128, 64, 1024, 16),
-               # up to 4 rows of 4-bit codes: the GEMV-shaped kernel (several K passes, pass tails,
-               # ragged N, and N smaller than a workgroup's rows)
+               # 1 and 2 rows: the GEMV-shaped kernel (several K passes, pass tails, ragged N, N
+               # smaller than a workgroup's rows); 3 and 4 rows: the matrix-core weight stream with
+               # the 8-row activation load, long rows (four quads in flight) and tiny K
                ("affine", 64, 4, 4160, 45), ("affine", 128, 1, 8320, 19), ("q4_0", 32, 3, 12320, 7),
                ("affine", 128, 2, 256, 3), ("q4_0", 32, 4, 32, 9),
-               # 5 to 8 rows at N >= 4096: the GEMV-shaped kernel with the activations in LDS
-               # (a ragged second K pass and two rows per wavefront; half the lanes past K; four
-               # passes of 128-groups with a half-filled last one; the largest K whose codes,
-               # scales and sums fill the 160 KB of LDS)
+               # 5 to 8 rows at N >= 4096 (the 8-row activation load; ragged K, N one past a
+               # workgroup's rows; long K with four quads in flight per wavefront)
                ("q4_0", 32, 5, 4192, 4099), ("affine", 64, 8, 2048, 4096), ("affine", 128, 7, 14336, 4100),
                ("q4_0", 32, 6, 8192, 4096), ("q4_0", 32, 8, 16384, 4096)]
 
