@@ -219,8 +219,8 @@ __global__ __launch_bounds__(BT, 2) void backward_partial_kernel(int M, int K, i
 // A workgroup of RW wavefronts owns a 2048-wide slice of K and a group of
 // weight rows; lane l owns the 16-byte code chunk l of the slice (32 weights,
 // so 32 output columns), and each wavefront walks its own sub-range of rows,
-// 4 per pass (2 with four activation rows) with the next pass's loads in
-// flight. Per row and column the work is one byte conversion and M
+// one (Q4_K) or two rows per pass with two passes of loads in flight. Per row
+// and column the work is one byte conversion and M
 // multiply-adds, acc += (dy * a) * q; the b term of w = a*q + b is the same
 // for the 16 (or 32) columns of a sub-block, so dy * b is summed once per row
 // and sub-block and added at the end. The wavefronts' sums are added in LDS in
@@ -230,11 +230,15 @@ constexpr int RW = 8;        // wavefronts per workgroup
 constexpr int KSL = 2048;    // K per workgroup (64 lanes x 32 weights)
 constexpr int KPAD = KSL + KSL / 32;  // LDS row of the wave reduction: one pad float per 32
 
-// rows per pass: 4, or 2 with four activation rows (registers)
-template <int MR>
-constexpr int rows_per_pass() { return MR >= 4 ? 2 : 4; }
+// Rows per pass (two passes in flight): 1 for Q4_K (a header and a code
+// chunk per row), 2 otherwise. Measured at 4096 x 14336, M = 1 / 2 / 4 (us):
+// Q4_K 14.4 / 17.2 / 24.4 with 1 row, 14.5 / 17.9-19.3 / 25.2 with 2, 16.4 /
+// 20.3 / 25.0 with 4; Q4_0 14.5 / 16.7 / 20.5 with 1, 12.6 / 15.0 / 20.6
+// with 2, 13.7 / 16.5 / 20.5 with 4; 8 rows was slower still.
+template <int FMTB, int MR>
+constexpr int rows_per_pass() { return FMTB == 2 ? 1 : 2; }
 
-template <int FMTB, int MR, int RR = rows_per_pass<MR>()>
+template <int FMTB, int MR, int RR = rows_per_pass<FMTB, MR>()>
 struct RowPass {
     uint4 q[RR];      // the lane's code chunk of each row
     uint4 h[RR];      // Q4_K: the chunk's block header
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(64 * RW) void backward_rows_kernel(int M, int K, in
     const uint32_t hoff = (uint32_t)(u >> 3) * Q4K_BYTES;
     const uint32_t soff = 2u * (uint32_t)((32 * u) / G);
     const int c = (u & 7) >> 1;  // Q4_K: 64-weight chunk of the block
-    constexpr int RR = rows_per_pass<MR>();
+    constexpr int RR = rows_per_pass<FMTB, MR>();
 
     auto load = [&](RowPass<FMTB, MR>& P, int r0) {
 #pragma unroll
